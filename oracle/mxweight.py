@@ -1,0 +1,75 @@
+"""MX block-32 FP8 weight encoding and the pages' ``[H // 4, I, 4]`` weight layout
+(oracle; test infrastructure only).
+
+[QKV-CTE] "Interface": ``weight`` is ``[H // 4, I, 4]`` FP8, "MX-contiguous": four consecutive
+contraction (H) elements of one output column share a 4-byte group, i.e. element (h, i) lives at
+flat byte ``((h // 4) * I + i) * 4 + h % 4``.  The block scales are one E8M0 exponent per 32
+consecutive H elements of a column, stored here as ``[H // 32, I]``.
+
+How a weight's E8M0 exponent is chosen is not stated on the pages; the plain reading taken is
+the OCP Microscaling (MX v1.0) shared-exponent rule: for a block with largest magnitude m,
+X = floor(log2 m) - 8 (8 = the largest E4M3 exponent), E = X + 127, and each element is encoded
+as E4M3_RNE_satfinite(w / 2^X).  An all-zero block gets E = 0 and zero codes.  The projection
+consumes whatever codes and exponents it is given, so this choice only shapes the inputs.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .codecs import e4m3_decode, e4m3_encode, e8m0_decode
+
+
+def _floor_log2(m: float) -> int:
+    """floor(log2 m) for a positive finite double, exactly (via frexp: m = f * 2^e, 0.5<=f<1)."""
+    _, e = math.frexp(m)
+    return e - 1
+
+
+def mx_weight_quantize(w):
+    """fp32 W [H, I] -> (codes uint8 [H // 4, I, 4], e8m0 uint8 [H // 32, I])."""
+    w = np.asarray(w, dtype=np.float32)
+    H, I = w.shape
+    if H % 32:
+        raise ValueError("H must be a multiple of 32")
+    if not np.isfinite(w).all():
+        raise ValueError("non-finite weight")
+    nb = H // 32
+    blocks = w.reshape(nb, 32, I)
+    amax = np.max(np.abs(blocks), axis=1).astype(np.float64)        # [nb, I]
+    E = np.zeros((nb, I), np.int64)
+    X = np.zeros((nb, I), np.int64)
+    nz = amax > 0
+    fl = np.vectorize(_floor_log2, otypes=[np.int64])(np.where(nz, amax, 1.0))
+    X = np.where(nz, fl - 8, 0)
+    E = np.where(nz, X + 127, 0)
+    if (E < 0).any() or (E > 254).any():
+        raise ValueError("block exponent outside E8M0 range")
+    # w / 2^X is exact in fp32 for these magnitudes (power-of-two scaling, no under/overflow
+    # for |w| >= 2^-100); computed in fp64 and narrowed exactly.
+    scaled = blocks.astype(np.float64) * np.ldexp(1.0, -X)[:, None, :]
+    scaled32 = scaled.astype(np.float32)
+    if not np.array_equal(scaled32.astype(np.float64), scaled):
+        raise ValueError("power-of-two rescale not exact")
+    q = e4m3_encode(scaled32)                                        # [nb, 32, I]
+    q = np.where(nz[:, None, :], q, 0).astype(np.uint8)
+    q_hi = q.reshape(H, I)                                           # natural [H, I]
+    codes = q_hi.reshape(H // 4, 4, I).transpose(0, 2, 1).copy()     # -> [H//4, I, 4]
+    return codes, E.astype(np.uint8)
+
+
+def mx_weight_decode(codes, e8m0) -> np.ndarray:
+    """(codes [H // 4, I, 4], e8m0 [H // 32, I]) -> float64 W [H, I] (exact)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    H4, I, four = c.shape
+    if four != 4:
+        raise ValueError("weight codes must be [H // 4, I, 4]")
+    H = H4 * 4
+    # element (h, i) = c[h // 4, i, h % 4]
+    nat = c.transpose(0, 2, 1).reshape(H, I)
+    vals = e4m3_decode(nat)
+    sc = e8m0_decode(np.asarray(e8m0, dtype=np.uint8))               # [H // 32, I]
+    if sc.shape != (H // 32, I):
+        raise ValueError("e8m0 scales must be [H // 32, I]")
+    return vals * np.repeat(sc, 32, axis=0)
