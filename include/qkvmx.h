@@ -1,0 +1,176 @@
+/*
+ * qkvmx.h -- C ABI of the MI355X (gfx950) fused MXFP8 QKV projection library.
+ *
+ * The operations follow two source pages:
+ *   [QKV-CTE]    "Kernel reference: qkv_cte -- Wan2.2 additions to the NKI Library QKV CTE MXFP8
+ *                projection" (sections "Upstream behavior", "Design 1)" .. "Design 5)",
+ *                "Interface").
+ *   [RMSNORM-MX] "RMSNorm MX Prefill Kernel API Reference" (parameters residual, eps,
+ *                unpadded_hidden_size, qmx_output_dtype, emit_norm_bf16).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library never frees or
+ *     retains them past the call.  Nothing is allocated on any call.
+ *   - Work is enqueued asynchronously on `stream` (NULL = the legacy default stream).  Calls on
+ *     one stream are ordered; the library keeps no mutable global state, so distinct streams may
+ *     call concurrently on distinct buffers.
+ *   - Every argument is validated on the host BEFORE any HIP call; a failed validation returns a
+ *     status and touches nothing.  qkvmx_last_error() then gives a one-line reason (per thread).
+ *   - A HIP launch error returns QKVMX_ERR_HIP.  Faults inside a kernel surface at the caller's
+ *     next synchronisation, as for any asynchronous HIP work.
+ *   - bf16 tensors are passed as uint16_t bit patterns; fp32 scales are IEEE binary32.
+ *   - T = B * S tokens: [B, S, ...] tensors of the pages are flattened to [T, ...].
+ */
+#ifndef QKVMX_H
+#define QKVMX_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QKVMX_OK = 0,
+  QKVMX_ERR_NULL = 1,         /* a required pointer is NULL                                  */
+  QKVMX_ERR_SHAPE = 2,        /* sizes inconsistent or outside the supported range           */
+  QKVMX_ERR_ALIGN = 3,        /* a pointer or stride violates the stated alignment           */
+  QKVMX_ERR_ARG = 4,          /* invalid flag / optional-argument combination                */
+  QKVMX_ERR_WORKSPACE = 5,    /* workspace missing or smaller than qkvmx_workspace_bytes()   */
+  QKVMX_ERR_UNSUPPORTED = 6,  /* well-formed request this build does not implement           */
+  QKVMX_ERR_HIP = 7           /* a HIP runtime call (launch) failed                          */
+} qkvmx_status;
+
+/* Pass-2 flags ([QKV-CTE] "Interface": qk_norm_pre_rope q_norm / k_norm, fused_rope). */
+enum {
+  QKVMX_NORM_Q = 1,       /* across-heads RMSNorm of the first (Q) segment                 */
+  QKVMX_NORM_K = 2,       /* across-heads RMSNorm of the K segment (needs num_kv_heads > 0)  */
+  QKVMX_FUSED_ROPE = 4    /* rotate-half RoPE on Q and K after the norm                      */
+};
+
+/* Output layouts ([QKV-CTE] "Interface": output_layout). */
+enum {
+  QKVMX_LAYOUT_BSD = 0    /* [T, I] row-major, I = (num_heads + 2 * num_kv_heads) * head_dim  */
+};
+
+/* Element types of the plain row quantiser's input. */
+enum { QKVMX_DTYPE_F32 = 0, QKVMX_DTYPE_BF16 = 1 };
+
+/* Static name of a status code. */
+const char* qkvmx_status_string(qkvmx_status s);
+
+/* Reason for the last non-OK status returned on the calling thread ("" if none). */
+const char* qkvmx_last_error(void);
+
+/* ------------------------------------------------------------------------------------------
+ * Weight preparation (one-time, like weight loading; not part of the per-token path).
+ * ------------------------------------------------------------------------------------------ */
+
+/* MX block-32 FP8 encoding of a natural-orientation fp32 weight W[H, I] (row-major).
+ * Writes the pages' layout ([QKV-CTE] "Interface", weight: "[H // 4, I, 4] FP8, MX-contiguous"):
+ * element (h, i) at byte ((h / 4) * I + i) * 4 + h % 4 of `w_h4_i_4` (H * I bytes), and one
+ * E8M0 exponent per 32 consecutive h of a column in `w_e8m0` ([H / 32, I] bytes).
+ * Exponent rule (OCP MX shared exponent, the plain reading; the pages do not fix it):
+ * X = floor(log2(max |w| of the block)) - 8, E = clamp(X + 127, 0, 254); code =
+ * E4M3 round-to-nearest-even, saturating, of w / 2^(E - 127); an all-zero block gets E = 0.
+ * Requires H % 32 == 0, H, I > 0.  Non-finite weights give unspecified codes. */
+qkvmx_status mx_weight_quantize(const float* w, int64_t H, int64_t I,
+                                uint8_t* w_h4_i_4, uint8_t* w_e8m0, hipStream_t stream);
+
+/* Bytes of the device-side packed weight for an [H, I] projection. */
+size_t qkv_weight_packed_bytes(int64_t H, int64_t I);
+
+/* Re-lays the pages' weight ([H / 4, I, 4] E4M3 codes + [H / 32, I] E8M0 exponents) into the
+ * layout the projection kernel reads: K-contiguous rows per output channel plus the exponents
+ * grouped per MFMA step.  `w_packed` (>= qkv_weight_packed_bytes(H, I) bytes, 256-byte aligned)
+ * is opaque; it depends only on (H, I).  Requires H % 32 == 0. */
+qkvmx_status qkv_weight_prepack(const uint8_t* w_h4_i_4, const uint8_t* w_e8m0, int64_t H,
+                                int64_t I, void* w_packed, size_t w_packed_bytes,
+                                hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Activation producers.
+ * ------------------------------------------------------------------------------------------ */
+
+/* ROW_MX row quantisation, the role of the pages' row_quantize_packed ([QKV-CTE] "Interface",
+ * packed_hidden: "[B, S, H + 4] FP8: H FP8 codes plus a 4-byte fp32 dequant scale tail").
+ * x: [T, H] fp32 or bf16 (x_dtype), row-major.  packed_out: [T, H + 4] bytes; per row
+ * s = fl32(max_h |x_h| / 448) (IEEE division), code_h = E4M3 round-to-nearest-even saturating of
+ * fl32(x_h / s), then s as little-endian fp32 at byte offset H.  A zero row gets s = 0 and zero
+ * codes.  Requires H % 32 == 0, H <= 16384; packed_out 4-byte aligned. */
+qkvmx_status row_quantize_packed(const void* x, int32_t x_dtype, int64_t T, int64_t H,
+                                 uint8_t* packed_out, hipStream_t stream);
+
+/* Fused residual add + RMSNorm + ROW_MX quantisation of bf16 hidden states
+ * ([RMSNORM-MX]; output in the ROW_MX packed layout the projection consumes).
+ *   r    = bf16_RNE(fp32(hidden) + fp32(residual))   -> residual_out   (r = hidden if no residual)
+ *   inv  = fp32(1 / sqrt(sum_h r_h^2 / Hu + eps))     (sum, sqrt and divide in fp64)
+ *   y_h  = fl32(fl32(r_h * inv) * gamma_h)            -> ROW_MX encode as row_quantize_packed
+ * hidden, residual, residual_out: [T, H] bf16; gamma: [H] bf16; packed_out: [T, H + 4].
+ * residual_out is required iff residual is given.  unpadded_H (Hu) in (0, H], 0 means H: the
+ * sum runs over all H columns, the mean divides by Hu.  Requires H % 32 == 0, H <= 16384. */
+qkvmx_status rmsnorm_mx_quantize(const uint16_t* hidden, const uint16_t* residual,
+                                 const uint16_t* gamma, float eps, int64_t T, int64_t H,
+                                 int64_t unpadded_H, uint16_t* residual_out, uint8_t* packed_out,
+                                 hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Pass 1: the projection ([QKV-CTE] "Upstream behavior", O[S, I] = A[S, H] @ W[H, I] + bias,
+ * I = (num_heads + 2 * num_kv_heads) * head_dim; "Design 1)" step a).
+ * ------------------------------------------------------------------------------------------ */
+
+/* Workspace bytes qkv_rowmx_project needs for its per-tile sums of squares. */
+size_t qkvmx_workspace_bytes(int64_t T, int64_t I);
+
+/* out[t, i] = bf16_RNE( a_scale[t] * c[i] * sum_h dec(a[t, h]) * dec(W[h, i]) * 2^(E[h/32, i]-127)
+ *                       + bias[i] )
+ * and, when ssq != NULL, ssq[t] = { sum over the Q columns of X^2, sum over the K columns of X^2 }
+ * over the fp32 values before rounding (V excluded; the K entry is 0 when num_kv_heads == 0).
+ *   a_codes       E4M3 codes of row t at a_codes + t * a_row_stride (H bytes).
+ *   a_scales      fp32 row scale of row t at a_scales + t * a_scale_stride (4-byte aligned).
+ *                 The pages' packed rows: a_scales = a_codes + H, both strides = H + 4.
+ *   w_packed      output of qkv_weight_prepack for this (H, I).
+ *   w_channel_scale  fp32 [I] per-output-channel scale ("weight_scales [1, I]"), NULL = 1.
+ *   bias          bf16 [I] or NULL.
+ *   layout        QKVMX_LAYOUT_BSD: out is [T, I] row-major bf16.
+ *   workspace     >= qkvmx_workspace_bytes(T, I) bytes, 16-byte aligned (required iff ssq).
+ * Requires T >= 1, H % 32 == 0, head_dim % 16 == 0, num_heads >= 1, num_kv_heads >= 0,
+ * a_row_stride >= H and a multiple of 4, a_codes 4-byte aligned, out 16-byte aligned. */
+qkvmx_status qkv_rowmx_project(const uint8_t* a_codes, int64_t a_row_stride,
+                               const uint8_t* a_scales, int64_t a_scale_stride,
+                               const void* w_packed, const float* w_channel_scale,
+                               const uint16_t* bias, int64_t T, int64_t H, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t layout,
+                               uint16_t* out, float* ssq, void* workspace, size_t ws_bytes,
+                               hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Pass 2: across-heads RMSNorm + rotate-half RoPE, in place on Q and K; V is neither read nor
+ * written ([QKV-CTE] "Design 1)" steps b and c, "Design 2)", "Design 5)").
+ * ------------------------------------------------------------------------------------------ */
+
+/* For a segment (Q: columns [0, Iq), K: [Iq, Iq + Ik)) with n heads, per token t:
+ *   r    = 1 / sqrt(ssq[t, seg] / (n * head_dim) + eps)              (when its NORM flag is set)
+ *   y_j  = x_j * gamma_j * r                                          (x_j otherwise)
+ *   RoPE: out_j = y_j * cos[t, j'] - y_{j+d/2} * sin[t, j']   for j' = j mod d < d/2,
+ *         out_j = y_j * cos[t, j'] + y_{j-d/2} * sin[t, j']   for j' >= d/2  (within each head)
+ * and out_j = y_j without QKVMX_FUSED_ROPE.  The result is stored as bf16 in place.
+ *   qkv       bf16 [T, I] as written by pass 1 (BSD), I = (num_heads + 2 * num_kv_heads) * d.
+ *   ssq       fp32 [T, 2] (pass 1's sums); required iff a NORM flag is set.
+ *   q_gamma   bf16 [num_heads * d], segment-wide; required iff QKVMX_NORM_Q.
+ *   k_gamma   bf16 [num_kv_heads * d]; required iff QKVMX_NORM_K, must be NULL otherwise.
+ *   cos_tab, sin_tab  fp32 [T, d] rotate-half caches; required iff QKVMX_FUSED_ROPE.
+ * num_kv_heads == 0 is a single-segment call: QKVMX_NORM_K is then an error.
+ * Requires head_dim % 16 == 0; qkv 16-byte aligned; tables and ssq 16-byte aligned. */
+qkvmx_status qk_norm_rope_apply(uint16_t* qkv, const float* ssq, const uint16_t* q_gamma,
+                                const uint16_t* k_gamma, const float* cos_tab,
+                                const float* sin_tab, int64_t T, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_dim, float eps,
+                                uint32_t flags, int32_t layout, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QKVMX_H */

@@ -8,8 +8,9 @@ consecutive H elements of a column, stored here as ``[H // 32, I]``.
 
 How a weight's E8M0 exponent is chosen is not stated on the pages; the plain reading taken is
 the OCP Microscaling (MX v1.0) shared-exponent rule: for a block with largest magnitude m,
-X = floor(log2 m) - 8 (8 = the largest E4M3 exponent), E = X + 127, and each element is encoded
-as E4M3_RNE_satfinite(w / 2^X).  An all-zero block gets E = 0 and zero codes.  The projection
+X = floor(log2 m) - 8 (8 = the largest E4M3 exponent), E = X + 127 clamped to the finite E8M0
+range [0, 254], and each element is encoded as E4M3_RNE_satfinite(w / 2^(E - 127)).  An
+all-zero block gets E = 0 and zero codes.  The projection
 consumes whatever codes and exponents it is given, so this choice only shapes the inputs.
 """
 from __future__ import annotations
@@ -38,14 +39,11 @@ def mx_weight_quantize(w):
     nb = H // 32
     blocks = w.reshape(nb, 32, I)
     amax = np.max(np.abs(blocks), axis=1).astype(np.float64)        # [nb, I]
-    E = np.zeros((nb, I), np.int64)
-    X = np.zeros((nb, I), np.int64)
     nz = amax > 0
     fl = np.vectorize(_floor_log2, otypes=[np.int64])(np.where(nz, amax, 1.0))
-    X = np.where(nz, fl - 8, 0)
-    E = np.where(nz, X + 127, 0)
-    if (E < 0).any() or (E > 254).any():
-        raise ValueError("block exponent outside E8M0 range")
+    # E = X + 127 clamped to the finite E8M0 range [0, 254]; the element scale is 2^(E - 127)
+    E = np.where(nz, np.clip(fl - 8 + 127, 0, 254), 0)
+    X = E - 127
     # w / 2^X is exact in fp32 for these magnitudes (power-of-two scaling, no under/overflow
     # for |w| >= 2^-100); computed in fp64 and narrowed exactly.
     scaled = blocks.astype(np.float64) * np.ldexp(1.0, -X)[:, None, :]

@@ -53,16 +53,19 @@ def _segment(x, gamma_bf16, r, cos, sin, d: int, norm: bool, rope: bool):
 
 
 def norm_rope(qkv_bf16, ssq, q_gamma_bf16, k_gamma_bf16, cos, sin, *, num_heads: int,
-              num_kv_heads: int, head_dim: int, eps: float, flags: int) -> np.ndarray:
+              num_kv_heads: int, head_dim: int, eps: float, flags: int,
+              values=None) -> np.ndarray:
     """qkv_bf16 uint16 [T, I] (as stored by pass 1) -> float64 [T, I] after pass 2.
 
     ``flags``: NORM_Q / NORM_K select the across-heads norm per segment, FUSED_ROPE applies
     rotate-half RoPE to both Q and K.  Columns outside Q and K come back bit-for-bit.
+    ``values`` (float64 [T, I]) replaces the stored bf16 input, e.g. with pass 1's unrounded
+    result to follow the whole chain without intermediate rounding.
     """
     d = head_dim
     Iq = num_heads * d
     Ik = num_kv_heads * d
-    x = bf16_to_f64(qkv_bf16)
+    x = bf16_to_f64(qkv_bf16) if values is None else np.asarray(values, dtype=np.float64)
     out = x.copy()
     rope = bool(flags & FUSED_ROPE)
     if rope and (cos is None or sin is None):

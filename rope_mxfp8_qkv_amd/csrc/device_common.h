@@ -1,0 +1,45 @@
+// Device-side helpers of the gfx950 kernels: bf16 and E4M3 conversions written from the
+// formats' bit layouts.  Internal header; not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qkvmx {
+
+// bf16 bits -> fp32 (exact widening).
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even.  Inputs are finite on every path.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two fp32 -> packed bf16x2 (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+}
+
+// fp32 -> FP8 E4M3 ("fn": max 448, no infinities), round to nearest even, saturating at +-448.
+// The sign bit is kept, so negative values that round to zero give 0x80.
+//  - |v| < 2^-6 lies on the subnormal grid of step 2^-9: code = rint(|v| * 2^9) (0..8; 8 is the
+//    smallest normal, 0x08, so the carry into the exponent field is automatic).
+//  - otherwise round the fp32 mantissa to 3 bits (RNE on the bit pattern) and rebias the
+//    exponent from 127 to 7; a mantissa carry moves into the exponent field by itself.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  float a = fminf(fabsf(v), 448.0f);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)rintf(a * 512.0f);
+  } else {
+    uint32_t b = __float_as_uint(a);
+    b += 0x7FFFFu + ((b >> 20) & 1u);
+    code = (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);
+  }
+  return code | sign;
+}
+
+}  // namespace qkvmx

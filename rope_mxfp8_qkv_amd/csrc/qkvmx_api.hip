@@ -1,0 +1,176 @@
+// C ABI of the library: host-side validation of every argument (before any HIP call), then the
+// kernel launches on the caller's stream.  Declared in include/qkvmx.h.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/qkvmx.h"
+#include "internal.h"
+
+using namespace qkvmx;
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+qkvmx_status fail(qkvmx_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+qkvmx_status ok() {
+  g_err[0] = '\0';
+  return QKVMX_OK;
+}
+
+qkvmx_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(QKVMX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int64_t kMaxRowH = 16384;             // row kernels keep a row in registers
+constexpr int64_t kMaxOffset = (int64_t)1 << 31; // 32-bit byte offsets in the projection
+
+}  // namespace
+
+extern "C" {
+
+const char* qkvmx_status_string(qkvmx_status s) {
+  switch (s) {
+    case QKVMX_OK: return "QKVMX_OK";
+    case QKVMX_ERR_NULL: return "QKVMX_ERR_NULL";
+    case QKVMX_ERR_SHAPE: return "QKVMX_ERR_SHAPE";
+    case QKVMX_ERR_ALIGN: return "QKVMX_ERR_ALIGN";
+    case QKVMX_ERR_ARG: return "QKVMX_ERR_ARG";
+    case QKVMX_ERR_WORKSPACE: return "QKVMX_ERR_WORKSPACE";
+    case QKVMX_ERR_UNSUPPORTED: return "QKVMX_ERR_UNSUPPORTED";
+    case QKVMX_ERR_HIP: return "QKVMX_ERR_HIP";
+  }
+  return "QKVMX_UNKNOWN_STATUS";
+}
+
+const char* qkvmx_last_error(void) { return g_err; }
+
+qkvmx_status mx_weight_quantize(const float* w, int64_t H, int64_t I, uint8_t* w_h4_i_4,
+                                uint8_t* w_e8m0, hipStream_t stream) {
+  if (!w || !w_h4_i_4 || !w_e8m0) return fail(QKVMX_ERR_NULL, "mx_weight_quantize: null pointer");
+  if (H <= 0 || I <= 0 || H % 32) return fail(QKVMX_ERR_SHAPE, "mx_weight_quantize: need H %% 32 == 0, H, I > 0");
+  if (H / 32 > 65535) return fail(QKVMX_ERR_UNSUPPORTED, "mx_weight_quantize: H too large");
+  if (!aligned(w, 4) || !aligned(w_h4_i_4, 4)) return fail(QKVMX_ERR_ALIGN, "mx_weight_quantize: w and codes must be 4-byte aligned");
+  return hip_status(launch_mx_weight_quantize(w, H, I, w_h4_i_4, w_e8m0, stream), "mx_weight_quantize");
+}
+
+size_t qkv_weight_packed_bytes(int64_t H, int64_t I) {
+  if (H <= 0 || I <= 0 || H % 32) return 0;
+  return packed_total_bytes(H, I);
+}
+
+qkvmx_status qkv_weight_prepack(const uint8_t* w_h4_i_4, const uint8_t* w_e8m0, int64_t H,
+                                int64_t I, void* w_packed, size_t w_packed_bytes,
+                                hipStream_t stream) {
+  if (!w_h4_i_4 || !w_e8m0 || !w_packed) return fail(QKVMX_ERR_NULL, "qkv_weight_prepack: null pointer");
+  if (H <= 0 || I <= 0 || H % 32) return fail(QKVMX_ERR_SHAPE, "qkv_weight_prepack: need H %% 32 == 0, H, I > 0");
+  if (H * I >= kMaxOffset) return fail(QKVMX_ERR_UNSUPPORTED, "qkv_weight_prepack: H * I must be < 2^31");
+  if (w_packed_bytes < packed_total_bytes(H, I))
+    return fail(QKVMX_ERR_SHAPE, "qkv_weight_prepack: w_packed_bytes %zu < %zu", w_packed_bytes, packed_total_bytes(H, I));
+  if (!aligned(w_h4_i_4, 4) || !aligned(w_packed, 256)) return fail(QKVMX_ERR_ALIGN, "qkv_weight_prepack: codes 4-byte, w_packed 256-byte aligned");
+  return hip_status(launch_weight_prepack(w_h4_i_4, w_e8m0, H, I, (uint8_t*)w_packed, stream), "qkv_weight_prepack");
+}
+
+qkvmx_status row_quantize_packed(const void* x, int32_t x_dtype, int64_t T, int64_t H,
+                                 uint8_t* packed_out, hipStream_t stream) {
+  if (!x || !packed_out) return fail(QKVMX_ERR_NULL, "row_quantize_packed: null pointer");
+  if (x_dtype != QKVMX_DTYPE_F32 && x_dtype != QKVMX_DTYPE_BF16) return fail(QKVMX_ERR_ARG, "row_quantize_packed: bad dtype");
+  if (T <= 0 || H <= 0 || H % 32) return fail(QKVMX_ERR_SHAPE, "row_quantize_packed: need T > 0, H %% 32 == 0");
+  if (H > kMaxRowH) return fail(QKVMX_ERR_UNSUPPORTED, "row_quantize_packed: H > %lld", (long long)kMaxRowH);
+  if (!aligned(x, 16) || !aligned(packed_out, 4)) return fail(QKVMX_ERR_ALIGN, "row_quantize_packed: x 16-byte, packed 4-byte aligned");
+  return hip_status(launch_row_quantize(x, x_dtype, T, H, packed_out, stream), "row_quantize_packed");
+}
+
+qkvmx_status rmsnorm_mx_quantize(const uint16_t* hidden, const uint16_t* residual,
+                                 const uint16_t* gamma, float eps, int64_t T, int64_t H,
+                                 int64_t unpadded_H, uint16_t* residual_out, uint8_t* packed_out,
+                                 hipStream_t stream) {
+  if (!hidden || !gamma || !packed_out) return fail(QKVMX_ERR_NULL, "rmsnorm_mx_quantize: null pointer");
+  if (residual && !residual_out) return fail(QKVMX_ERR_ARG, "rmsnorm_mx_quantize: residual_out is required with a residual");
+  if (!residual && residual_out) return fail(QKVMX_ERR_ARG, "rmsnorm_mx_quantize: residual_out given without a residual");
+  if (T <= 0 || H <= 0 || H % 32) return fail(QKVMX_ERR_SHAPE, "rmsnorm_mx_quantize: need T > 0, H %% 32 == 0");
+  if (unpadded_H < 0 || unpadded_H > H) return fail(QKVMX_ERR_SHAPE, "rmsnorm_mx_quantize: unpadded_H outside [0, H]");
+  if (!(eps >= 0.0f)) return fail(QKVMX_ERR_ARG, "rmsnorm_mx_quantize: eps must be >= 0");
+  if (H > kMaxRowH) return fail(QKVMX_ERR_UNSUPPORTED, "rmsnorm_mx_quantize: H > %lld", (long long)kMaxRowH);
+  if (!aligned(hidden, 16) || !aligned(gamma, 16) || (residual && !aligned(residual, 16)) ||
+      (residual_out && !aligned(residual_out, 16)) || !aligned(packed_out, 4))
+    return fail(QKVMX_ERR_ALIGN, "rmsnorm_mx_quantize: bf16 tensors 16-byte, packed 4-byte aligned");
+  const int64_t Hu = unpadded_H ? unpadded_H : H;
+  return hip_status(launch_rmsnorm_quantize(hidden, residual, gamma, eps, T, H, Hu, residual_out,
+                                            packed_out, stream), "rmsnorm_mx_quantize");
+}
+
+size_t qkvmx_workspace_bytes(int64_t T, int64_t I) {
+  if (T <= 0 || I <= 0) return 0;
+  return workspace_total_bytes(T, I);
+}
+
+qkvmx_status qkv_rowmx_project(const uint8_t* a_codes, int64_t a_row_stride,
+                               const uint8_t* a_scales, int64_t a_scale_stride,
+                               const void* w_packed, const float* w_channel_scale,
+                               const uint16_t* bias, int64_t T, int64_t H, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t layout,
+                               uint16_t* out, float* ssq, void* workspace, size_t ws_bytes,
+                               hipStream_t stream) {
+  if (!a_codes || !a_scales || !w_packed || !out) return fail(QKVMX_ERR_NULL, "qkv_rowmx_project: null pointer");
+  if (ssq && !workspace) return fail(QKVMX_ERR_WORKSPACE, "qkv_rowmx_project: ssq requested without a workspace");
+  if (T <= 0 || H <= 0 || H % 32) return fail(QKVMX_ERR_SHAPE, "qkv_rowmx_project: need T > 0, H %% 32 == 0");
+  if (num_heads < 1 || num_kv_heads < 0 || head_dim <= 0 || head_dim % 16)
+    return fail(QKVMX_ERR_SHAPE, "qkv_rowmx_project: need num_heads >= 1, num_kv_heads >= 0, head_dim %% 16 == 0");
+  if (layout != QKVMX_LAYOUT_BSD) return fail(QKVMX_ERR_UNSUPPORTED, "qkv_rowmx_project: only the BSD layout is built");
+  if (a_row_stride < H || a_row_stride % 4 || a_scale_stride <= 0 || a_scale_stride % 4)
+    return fail(QKVMX_ERR_SHAPE, "qkv_rowmx_project: a_row_stride >= H and strides multiples of 4");
+  const int64_t I = (int64_t)(num_heads + 2 * (int64_t)num_kv_heads) * head_dim;
+  if (H * I >= kMaxOffset || (T - 1) * a_row_stride + H >= kMaxOffset)
+    return fail(QKVMX_ERR_UNSUPPORTED, "qkv_rowmx_project: weight or activation span must be < 2^31 bytes");
+  if (ssq && ws_bytes < workspace_total_bytes(T, I))
+    return fail(QKVMX_ERR_WORKSPACE, "qkv_rowmx_project: workspace %zu < %zu bytes", ws_bytes, workspace_total_bytes(T, I));
+  if (!aligned(a_codes, 4) || !aligned(a_scales, 4) || !aligned(w_packed, 256) ||
+      (w_channel_scale && !aligned(w_channel_scale, 16)) || (bias && !aligned(bias, 8)) ||
+      !aligned(out, 16) || (ssq && (!aligned(ssq, 8) || !aligned(workspace, 16))))
+    return fail(QKVMX_ERR_ALIGN, "qkv_rowmx_project: alignment (codes/scales 4, w_packed 256, channel scale 16, bias 8, out 16, ssq 8, workspace 16)");
+  const int64_t Iq = (int64_t)num_heads * head_dim, Ik = (int64_t)num_kv_heads * head_dim;
+  return hip_status(launch_project(a_codes, a_row_stride, a_scales, a_scale_stride,
+                                   (const uint8_t*)w_packed, w_channel_scale, bias, T, H, I, Iq,
+                                   Ik, out, ssq, (float*)workspace, stream), "qkv_rowmx_project");
+}
+
+qkvmx_status qk_norm_rope_apply(uint16_t* qkv, const float* ssq, const uint16_t* q_gamma,
+                                const uint16_t* k_gamma, const float* cos_tab,
+                                const float* sin_tab, int64_t T, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_dim, float eps,
+                                uint32_t flags, int32_t layout, hipStream_t stream) {
+  if (!qkv) return fail(QKVMX_ERR_NULL, "qk_norm_rope_apply: null qkv");
+  if (flags & ~(uint32_t)(QKVMX_NORM_Q | QKVMX_NORM_K | QKVMX_FUSED_ROPE))
+    return fail(QKVMX_ERR_ARG, "qk_norm_rope_apply: unknown flag bits");
+  if (T <= 0 || num_heads < 1 || num_kv_heads < 0 || head_dim <= 0 || head_dim % 16)
+    return fail(QKVMX_ERR_SHAPE, "qk_norm_rope_apply: need T > 0, num_heads >= 1, num_kv_heads >= 0, head_dim %% 16 == 0");
+  if (layout != QKVMX_LAYOUT_BSD) return fail(QKVMX_ERR_UNSUPPORTED, "qk_norm_rope_apply: only the BSD layout is built");
+  if ((flags & QKVMX_FUSED_ROPE) && (!cos_tab || !sin_tab))
+    return fail(QKVMX_ERR_ARG, "qk_norm_rope_apply: QKVMX_FUSED_ROPE needs cos_tab and sin_tab");
+  if (num_kv_heads == 0 && ((flags & QKVMX_NORM_K) || k_gamma))
+    return fail(QKVMX_ERR_ARG, "qk_norm_rope_apply: no K segment when num_kv_heads == 0 (omit k_gamma and QKVMX_NORM_K)");
+  if ((flags & QKVMX_NORM_Q) && !q_gamma) return fail(QKVMX_ERR_ARG, "qk_norm_rope_apply: QKVMX_NORM_Q needs q_gamma");
+  if ((flags & QKVMX_NORM_K) && !k_gamma) return fail(QKVMX_ERR_ARG, "qk_norm_rope_apply: QKVMX_NORM_K needs k_gamma");
+  if (!(flags & QKVMX_NORM_K) && k_gamma) return fail(QKVMX_ERR_ARG, "qk_norm_rope_apply: k_gamma given without QKVMX_NORM_K");
+  if ((flags & (QKVMX_NORM_Q | QKVMX_NORM_K)) && !ssq) return fail(QKVMX_ERR_ARG, "qk_norm_rope_apply: the norm needs ssq");
+  if (!(eps >= 0.0f)) return fail(QKVMX_ERR_ARG, "qk_norm_rope_apply: eps must be >= 0");
+  if (!aligned(qkv, 16) || (ssq && !aligned(ssq, 8)) || (q_gamma && !aligned(q_gamma, 16)) ||
+      (k_gamma && !aligned(k_gamma, 16)) || (cos_tab && !aligned(cos_tab, 16)) ||
+      (sin_tab && !aligned(sin_tab, 16)))
+    return fail(QKVMX_ERR_ALIGN, "qk_norm_rope_apply: qkv/gamma/tables 16-byte, ssq 8-byte aligned");
+  return hip_status(launch_norm_rope(qkv, ssq, q_gamma, k_gamma, cos_tab, sin_tab, T, num_heads,
+                                     num_kv_heads, head_dim, eps, flags, stream), "qk_norm_rope_apply");
+}
+
+}  // extern "C"

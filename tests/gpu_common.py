@@ -1,0 +1,142 @@
+"""Shared pieces of the GPU parity tests: inputs from the seeded recipe, expected values from the
+oracle (never from the HIP path), the library calls through the C ABI, and the comparison rules.
+
+Tolerances
+  * codes, scales, residual sums, V columns: bit-exact.
+  * bf16 outputs: |gpu - ref| <= 1e-2 * |ref| + 1e-3 elementwise, ref = unrounded fp64 oracle.
+  * per-token sums of squares: |gpu - ref| <= 2e-3 * ref.
+  * pass 2 checked end to end (from the same A and W) against the unrounded fp64 chain: the bf16
+    rounding of pass 1's stored output (at most 2^-8 relative per element) enters both lanes of a
+    RoPE pair, so the bound adds 2^-8 * r * (|g_j x_j| + |g_p x_p|) for lane j and its partner p.
+"""
+from __future__ import annotations
+
+import dataclasses
+import os
+import sys
+from typing import Optional
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle                      # noqa: E402
+import synth                       # noqa: E402
+from oracle import codecs          # noqa: E402
+
+REL, ABS, SSQ_REL = 1e-2, 1e-3, 2e-3
+
+
+def torch_dev():
+    import torch
+    if not torch.cuda.is_available():
+        import pytest
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def to_dev(a: np.ndarray, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def bf16_dev(bits: np.ndarray, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def bf16_host(t) -> np.ndarray:
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_close(gpu_bits: np.ndarray, ref: np.ndarray, what: str, extra=None):
+    """Elementwise |gpu - ref| <= REL |ref| + ABS (+ extra)."""
+    g = codecs.bf16_to_f64(gpu_bits)
+    tol = REL * np.abs(ref) + ABS
+    if extra is not None:
+        tol = tol + extra
+    bad = np.abs(g - ref) > tol
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; first "
+                             f"{[(tuple(i), g[tuple(i)], ref[tuple(i)]) for i in idx]}")
+
+
+def check_ssq(gpu: np.ndarray, ref: np.ndarray, what: str):
+    bad = np.abs(gpu.astype(np.float64) - ref) > SSQ_REL * np.abs(ref) + 1e-30
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {bad.sum()} sums outside 2e-3; first "
+                             f"{[(tuple(i), gpu[tuple(i)], ref[tuple(i)]) for i in idx]}")
+
+
+def check_equal(gpu: np.ndarray, ref: np.ndarray, what: str):
+    if not np.array_equal(gpu, ref):
+        bad = np.argwhere(gpu != ref)
+        idx = bad[:5]
+        raise AssertionError(f"{what}: {len(bad)} mismatches; first "
+                             f"{[(tuple(i), gpu[tuple(i)], ref[tuple(i)]) for i in idx]}")
+
+
+def propagated_bound(X: np.ndarray, ssq: np.ndarray, gq, gk, nq, nkv, d, eps, norm_q, norm_k,
+                     rope: bool) -> np.ndarray:
+    """2^-8 * r * (|g_j x_j| + |g_p x_p|) over Q/K lanes (0 elsewhere); see module docstring."""
+    out = np.zeros_like(X)
+    h = d // 2
+    for lo, n, g, col, on in ((0, nq, gq, 0, norm_q), (nq * d, nkv, gk, 1, norm_k)):
+        if n == 0:
+            continue
+        w = n * d
+        seg = X[:, lo:lo + w]
+        gv = codecs.bf16_to_f64(g) if (on and g is not None) else np.ones(w)
+        r = oracle.inv_rms(ssq[:, col], n, d, eps) if on else np.ones(X.shape[0])
+        a = np.abs(seg * gv[None, :]) * r[:, None]
+        if rope:
+            ah = a.reshape(-1, n, 2, h)
+            a = (ah + ah[:, :, ::-1, :]).reshape(-1, w)
+        out[:, lo:lo + w] = 2.0 ** -8 * a
+    return out
+
+
+@dataclasses.dataclass
+class ProjInputs:
+    p: synth.Projection
+    x: np.ndarray              # fp32 activations [T, H]
+    packed: np.ndarray         # oracle ROW_MX rows [T, H + 4]
+    w_codes: np.ndarray        # [H/4, I, 4]
+    w_e8m0: np.ndarray         # [H/32, I]
+    bias: np.ndarray           # bf16 bits [I]
+    gq: Optional[np.ndarray]
+    gk: Optional[np.ndarray]
+    cos: Optional[np.ndarray]
+    sin: Optional[np.ndarray]
+
+
+def make_inputs(p: synth.Projection, with_bias=True) -> ProjInputs:
+    x = synth.activation(p)
+    w = synth.weight(p)
+    codes, e8 = oracle.mx_weight_quantize(w)
+    cos, sin = synth.rope_tables(p)
+    return ProjInputs(p, x, oracle.rowmx_quantize(x), codes, e8,
+                      synth.bias_bf16(p) if with_bias else None,
+                      synth.gamma_bf16(p, "q"), synth.gamma_bf16(p, "k"), cos, sin)
+
+
+def flags_of(p: synth.Projection) -> int:
+    from rope_mxfp8_qkv_amd import NORM_Q, NORM_K, FUSED_ROPE
+    f = 0
+    if p.norm_q:
+        f |= NORM_Q
+    if p.norm_k and p.num_kv_heads > 0:
+        f |= NORM_K
+    if p.rope:
+        f |= FUSED_ROPE
+    return f
+
+
+def custom_projection(name, T, H, nq, nkv, d, rope="1d", seed=99):
+    return synth.Projection(name, seed, T=T, H=H, num_heads=nq, num_kv_heads=nkv, head_dim=d,
+                            rope=rope, norm_q=True, norm_k=nkv > 0)

@@ -1,0 +1,119 @@
+"""The C-ABI library: it loads, exports every function include/qkvmx.h declares with the
+binding's signatures, and rejects bad arguments on the host before any HIP call (these status
+paths run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qkvmx.h")
+
+
+def _lib():
+    from rope_mxfp8_qkv_amd import _abi
+    if not os.path.exists(_abi.lib_path()):
+        pytest.fail("libqkvmx.so is not built (run `python -m rope_mxfp8_qkv_amd.build`)")
+    return _abi.lib()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+\*?([a-z_][a-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_functions_exported_and_bound():
+    from rope_mxfp8_qkv_amd import _abi
+    L = _lib()
+    names = _declared_functions()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in _abi.SIGNATURES, n
+    assert set(_abi.SIGNATURES) == set(names)
+
+
+def test_status_strings():
+    from rope_mxfp8_qkv_amd import _abi
+    _lib()
+    assert _abi.status_string(0) == "QKVMX_OK"
+    assert _abi.status_string(7) == "QKVMX_ERR_HIP"
+
+
+def test_size_queries():
+    L = _lib()
+    assert L.qkv_weight_packed_bytes(5120, 15360) >= 5120 * 15360 + 15360 * 20 * 8
+    assert L.qkv_weight_packed_bytes(100, 16) == 0           # H % 32 != 0
+    assert L.qkvmx_workspace_bytes(75600, 15360) == 120 * 75600 * 8
+    assert L.qkvmx_workspace_bytes(0, 16) == 0
+
+
+P = 0x10000   # a fake, well-aligned device address: validation fails before it is used
+
+
+def _proj(L, **kw):
+    a = dict(a_codes=P, a_row_stride=260, a_scales=P + 256, a_scale_stride=260, w_packed=P,
+             w_channel_scale=None, bias=None, T=4, H=256, num_heads=2, num_kv_heads=2,
+             head_dim=64, layout=0, out=P, ssq=None, workspace=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return L.qkv_rowmx_project(*a.values())
+
+
+def _nr(L, **kw):
+    a = dict(qkv=P, ssq=P, q_gamma=P, k_gamma=P, cos=P, sin=P, T=4, num_heads=2, num_kv_heads=2,
+             head_dim=64, eps=1e-6, flags=7, layout=0, stream=None)
+    a.update(kw)
+    return L.qk_norm_rope_apply(*a.values())
+
+
+def test_projection_validation():
+    from rope_mxfp8_qkv_amd import _abi
+    L = _lib()
+    assert _proj(L, a_codes=None) == 1
+    assert _proj(L, H=100, a_row_stride=104, a_scale_stride=104) == 2
+    assert _proj(L, head_dim=40) == 2
+    assert _proj(L, T=0) == 2
+    assert _proj(L, layout=1) == 6
+    assert _proj(L, a_row_stride=258) == 2
+    assert _proj(L, ssq=P) == 5                                   # ssq without workspace
+    assert _proj(L, ssq=P, workspace=P, ws_bytes=8) == 5          # workspace too small
+    assert _proj(L, out=P + 2) == 3
+    assert _proj(L, a_scales=P + 2) == 3
+    assert _proj(L, w_packed=P + 16) == 3
+    assert "alignment" in _abi.last_error()
+
+
+def test_norm_rope_validation():
+    L = _lib()
+    assert _nr(L, qkv=None) == 1
+    assert _nr(L, cos=None) == 4                                  # RoPE without tables
+    assert _nr(L, num_kv_heads=0) == 4                            # k_gamma with no K segment
+    assert _nr(L, num_kv_heads=0, k_gamma=None) == 4              # NORM_K with no K segment
+    assert _nr(L, flags=1 | 4, k_gamma=P) == 4                    # k_gamma without NORM_K
+    assert _nr(L, q_gamma=None) == 4
+    assert _nr(L, ssq=None) == 4
+    assert _nr(L, flags=8) == 4
+    assert _nr(L, head_dim=24) == 2
+    assert _nr(L, eps=-1.0) == 4
+    assert _nr(L, layout=1) == 6
+    assert _nr(L, qkv=P + 8) == 3
+
+
+def test_producer_and_weight_validation():
+    L = _lib()
+    assert L.rmsnorm_mx_quantize(P, P, P, 1e-6, 4, 256, 0, None, P, None) == 4   # no residual_out
+    assert L.rmsnorm_mx_quantize(P, None, P, 1e-6, 4, 256, 0, P, P, None) == 4   # stray residual_out
+    assert L.rmsnorm_mx_quantize(P, None, P, 1e-6, 4, 250, 0, None, P, None) == 2
+    assert L.rmsnorm_mx_quantize(P, None, P, 1e-6, 4, 256, 257, None, P, None) == 2
+    assert L.rmsnorm_mx_quantize(P, None, P, 1e-6, 4, 32768, 0, None, P, None) == 6
+    assert L.rmsnorm_mx_quantize(None, None, P, 1e-6, 4, 256, 0, None, P, None) == 1
+    assert L.row_quantize_packed(P, 5, 4, 256, P, None) == 4
+    assert L.row_quantize_packed(P, 0, 4, 96 + 8, P, None) == 2
+    assert L.row_quantize_packed(P + 4, 0, 4, 256, P, None) == 3
+    assert L.mx_weight_quantize(P, 100, 16, P, P, None) == 2
+    assert L.qkv_weight_prepack(P, P, 256, 16, P, 10, None) == 2                 # buffer too small
+    assert L.qkv_weight_prepack(P, P, 256, 16, P + 64, 1 << 20, None) == 3
