@@ -1,0 +1,267 @@
+"""Throughput of the fused MXFP8 QKV path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input already resident in
+HBM: residual add + RMSNorm + ROW_MX quantisation of the bf16 hidden states, the ROW_MX x MX
+FP8 QKV projection with its fused dequant / bias / sum-of-squares epilogue, and the in-place
+across-heads RMSNorm + 3-axis rotate-half RoPE on Q and K.  Workload: the full video shape,
+T = 75600 tokens (21 x 45 x 80 grid), H = 5120, 40 Q + 40 KV heads x 128 (I = 15360).
+
+Prints ONE JSON line.  ``value`` is the projection's algorithmic TFLOP/s over the whole step
+(2 * T * H * I / step time).  Per-kernel durations come from HIP events recorded on the stream
+the library launches on, averaged over the timed steps.  ``cpu_baseline`` times the CPU oracle
+(NumPy, fp64) on a bounded row sample of the same workload on this host.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5|3|2] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "QKV proj TFLOP/s (% MXFP8 MFMA peak) + norm/RoPE GB/s, S=75600 H=5120"
+PEAK_MXFP8_TFLOPS = 5000.0          # MI355X dense MXFP8 MFMA
+PEAK_HBM_GBS = 8000.0               # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=5, choices=[2, 3, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=384)
+    return ap.parse_args()
+
+
+def gen_inputs(cid, dev):
+    import torch
+
+    import synth
+    cfg = synth.CONFIGS[cid]
+    p = cfg.calls[0]
+    t0 = time.time()
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def dv(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    inp = {"p": p, "producer": cfg.producer}
+    if cfg.producer:
+        hid, res, gam = synth.producer_inputs(cid, p.T, p.H)
+        inp.update(hid=bf(hid), res=bf(res), pgamma=bf(gam))
+        del hid, res
+    else:
+        inp["x"] = dv(synth.activation(p))
+    inp["w"] = dv(synth.weight(p))
+    inp["bias"] = bf(synth.bias_bf16(p))
+    inp["gq"] = bf(synth.gamma_bf16(p, "q"))
+    inp["gk"] = bf(synth.gamma_bf16(p, "k"))
+    cos, sin = synth.rope_tables(p)
+    inp["cos"], inp["sin"] = dv(cos), dv(sin)
+    inp["gen_s"] = time.time() - t0
+    return inp
+
+
+def algorithmic_bytes(p, producer: bool):
+    """Per-kernel algorithmic HBM bytes (each input read once, each output written once)."""
+    T, H, Iq, Ik, d = p.T, p.H, p.Iq, p.Ik, p.head_dim
+    nr = 4 * T * (Iq + Ik) + (8 * T * d if p.rope else 0) + 8 * T + 2 * (Iq + Ik)
+    prod = 4 * T * H + 2 * T * H + T * (H + 4) + 2 * H if producer else 0
+    return {"norm_rope": nr, "producer": prod}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def run_gpu(args):
+    import torch
+
+    import rope_mxfp8_qkv_amd as q
+    dev = torch.device("cuda:0")
+    log(f"generating inputs for config {args.config}")
+    inp = gen_inputs(args.config, dev)
+    log(f"inputs ready in {inp['gen_s']:.1f} s")
+    p = inp["p"]
+    T, H, I = p.T, p.H, p.I
+    stream = torch.cuda.current_stream()
+
+    # weight preparation (one-time, untimed)
+    codes = torch.empty((H // 4, I, 4), dtype=torch.uint8, device=dev)
+    e8 = torch.empty((H // 32, I), dtype=torch.uint8, device=dev)
+    q.mx_weight_quantize(inp["w"], codes, e8)
+    wp = q.prepare_weight(codes, e8, H, I)
+    del inp["w"], codes, e8
+
+    packed = torch.empty((T, H + 4), dtype=torch.uint8, device=dev)
+    res_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if inp["producer"] else None
+    out = torch.empty((T, I), dtype=torch.bfloat16, device=dev)
+    ssq = torch.empty((T, 2), dtype=torch.float32, device=dev)
+    ws = torch.empty(q.qkvmx_workspace_bytes(T, I), dtype=torch.uint8, device=dev)
+    flags = q.NORM_Q | q.NORM_K | q.FUSED_ROPE
+    if not inp["producer"]:
+        q.row_quantize_packed(inp["x"], packed)     # activations fixed for the whole run
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        if inp["producer"]:
+            q.rmsnorm_mx_quantize(inp["hid"], inp["pgamma"], 1e-6, packed, residual=inp["res"],
+                                  residual_out=res_out)
+        if ev:
+            ev[1].record(stream)
+        q.qkv_rowmx_project(packed, wp, out, H=H, num_heads=p.num_heads,
+                            num_kv_heads=p.num_kv_heads, head_dim=p.head_dim, bias=inp["bias"],
+                            ssq=ssq, workspace=ws)
+        if ev:
+            ev[2].record(stream)
+        q.qk_norm_rope_apply(out, num_heads=p.num_heads, num_kv_heads=p.num_kv_heads,
+                             head_dim=p.head_dim, eps=1e-6, flags=flags, ssq=ssq,
+                             q_gamma=inp["gq"], k_gamma=inp["gk"], cos=inp["cos"], sin=inp["sin"])
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                      for e in evs])
+    ms = stage.mean(axis=0)          # producer, projection (+ sum reduce), norm/rope
+    ms_step = wall * 1e3 / args.steps
+    flops = 2.0 * T * H * I
+    nbytes = algorithmic_bytes(p, inp["producer"])
+    proj_tflops = flops / (ms[1] * 1e-3) / 1e12
+    res = {
+        "ms_per_step": ms_step,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "stage_ms": {"producer": float(ms[0]), "projection": float(ms[1]),
+                     "norm_rope": float(ms[2])},
+        "projection_tflops": proj_tflops,
+        "norm_rope_gbs": nbytes["norm_rope"] / (ms[2] * 1e-3) / 1e9,
+        "producer_gbs": (nbytes["producer"] / (ms[0] * 1e-3) / 1e9) if inp["producer"] else None,
+        "flops": flops,
+        "bytes": nbytes,
+        "gen_s": inp["gen_s"],
+        "p": p,
+        "producer": inp["producer"],
+    }
+    return res
+
+
+def cpu_baseline(cid, rows_n):
+    """The oracle, as it stands, on the first ``rows_n`` tokens of the same workload."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:                                        # pragma: no cover
+        threads = 1
+    cfg = synth.CONFIGS[cid]
+    p = cfg.calls[0]
+    rows = np.arange(rows_n)
+    w = synth.weight(p)
+    if cfg.producer:
+        hid, res, gam = synth.producer_inputs(cid, p.T, p.H, row_idx=rows)
+    else:
+        x = synth.activation(p, row_idx=rows)
+    cos, sin = synth.rope_tables(p, rows)
+    bias, gq, gk = synth.bias_bf16(p), synth.gamma_bf16(p, "q"), synth.gamma_bf16(p, "k")
+    wc, we = oracle.mx_weight_quantize(w)                   # weight prep: untimed, as on the GPU
+    t0 = time.perf_counter()
+    if cfg.producer:
+        _, packed, _ = oracle.rmsnorm_rowmx(hid, res, gam, 1e-6)
+    else:
+        packed = oracle.rowmx_quantize(x)
+    codes, sA = oracle.rowmx_unpack(packed, p.H)
+    X, ssq = oracle.project(codes, sA, wc, we, None, bias, num_heads=p.num_heads,
+                            num_kv_heads=p.num_kv_heads, head_dim=p.head_dim)
+    xb = oracle.f64_to_bf16(X)
+    oracle.norm_rope(xb, ssq, gq, gk, cos, sin, num_heads=p.num_heads,
+                     num_kv_heads=p.num_kv_heads, head_dim=p.head_dim, eps=1e-6, flags=7)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows_n * p.H * p.I
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {rows_n} of {p.T} tokens, whole step (producer/quantise, "
+                      f"fp64 projection incl. weight decode, norm+RoPE); {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+                                   "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        sys.exit(2)
+    r = run_gpu(args)
+    p = r["p"]
+    log(f"gpu: {r['ms_per_step']:.3f} ms/step, stages {r['stage_ms']}")
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_rows} rows")
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.config, args.cpu_rows)
+    ach = r["projection_tflops"]
+    line = {
+        "metric": METRIC,
+        "value": r["value"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8 (e4m3 x e4m3 -> fp32 MFMA), fp32 norm/RoPE, bf16 I/O",
+        "data": "synthetic",
+        "config": {
+            "workload": ("producer + QKV projection + across-heads norm + 3-axis RoPE"
+                         if r["producer"] else "QKV projection + across-heads norm + RoPE"),
+            "T": p.T, "H": p.H, "I": p.I, "num_heads": p.num_heads,
+            "num_kv_heads": p.num_kv_heads, "head_dim": p.head_dim,
+            "grid": list(p.grid) if p.grid else None, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "project_kernel (+ ssq_reduce_kernel)",
+            "bound": "mfma",
+            "achieved": ach,
+            "peak": PEAK_MXFP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": ach / PEAK_MXFP8_TFLOPS,
+            "traffic": None,
+        },
+        "stages": {
+            "ms": r["stage_ms"],
+            "projection_tflops": r["projection_tflops"],
+            "norm_rope_gbs": r["norm_rope_gbs"],
+            "norm_rope_hbm_frac": r["norm_rope_gbs"] / PEAK_HBM_GBS,
+            "producer_gbs": r["producer_gbs"],
+            "producer_hbm_frac": (r["producer_gbs"] / PEAK_HBM_GBS) if r["producer_gbs"] else None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

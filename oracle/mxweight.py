@@ -28,12 +28,30 @@ def _floor_log2(m: float) -> int:
     return e - 1
 
 
-def mx_weight_quantize(w):
-    """fp32 W [H, I] -> (codes uint8 [H // 4, I, 4], e8m0 uint8 [H // 32, I])."""
+def mx_weight_quantize(w, rows_per_chunk: int = 256):
+    """fp32 W [H, I] -> (codes uint8 [H // 4, I, 4], e8m0 uint8 [H // 32, I]).
+
+    Processed ``rows_per_chunk`` rows of H at a time (whole 32-row blocks) to bound the memory
+    of the temporaries; the blocks are independent, so the result does not depend on it.
+    """
     w = np.asarray(w, dtype=np.float32)
     H, I = w.shape
     if H % 32:
         raise ValueError("H must be a multiple of 32")
+    step = max(32, rows_per_chunk - rows_per_chunk % 32)
+    codes = np.empty((H // 4, I, 4), np.uint8)
+    e8 = np.empty((H // 32, I), np.uint8)
+    for h0 in range(0, H, step):
+        h1 = min(H, h0 + step)
+        c, e = _quantize_rows(w[h0:h1])
+        codes[h0 // 4:h1 // 4] = c
+        e8[h0 // 32:h1 // 32] = e
+    return codes, e8
+
+
+def _quantize_rows(w):
+    """One group of whole 32-row blocks: fp32 [h, I] -> ([h // 4, I, 4], [h // 32, I])."""
+    H, I = w.shape
     if not np.isfinite(w).all():
         raise ValueError("non-finite weight")
     nb = H // 32

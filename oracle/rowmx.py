@@ -17,11 +17,21 @@ import numpy as np
 from .codecs import e4m3_encode, E4M3_MAX
 
 
-def rowmx_quantize(y) -> np.ndarray:
-    """fp32 [T, H] -> packed uint8 [T, H + 4]."""
+def rowmx_quantize(y, rows_per_chunk: int = 1024) -> np.ndarray:
+    """fp32 [T, H] -> packed uint8 [T, H + 4] (rows are independent; processed in chunks of
+    ``rows_per_chunk`` to bound the memory of the temporaries)."""
     y = np.asarray(y, dtype=np.float32)
     if y.ndim != 2:
         raise ValueError("rows must be 2-D")
+    if y.shape[0] > rows_per_chunk:
+        out = np.empty((y.shape[0], y.shape[1] + 4), np.uint8)
+        for r0 in range(0, y.shape[0], rows_per_chunk):
+            out[r0:r0 + rows_per_chunk] = _quantize_rows(y[r0:r0 + rows_per_chunk])
+        return out
+    return _quantize_rows(y)
+
+
+def _quantize_rows(y) -> np.ndarray:
     if not np.isfinite(y).all():
         raise ValueError("non-finite activation")
     T, H = y.shape
