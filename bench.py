@@ -109,7 +109,7 @@ def run_gpu(args):
     res_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if inp["producer"] else None
     out = torch.empty((T, I), dtype=torch.bfloat16, device=dev)
     ssq = torch.empty((T, 2), dtype=torch.float32, device=dev)
-    ws = torch.empty(q.qkvmx_workspace_bytes(T, I), dtype=torch.uint8, device=dev)
+    ws = torch.empty(q.qkvmx_workspace_bytes(T, H, I), dtype=torch.uint8, device=dev)
     flags = q.NORM_Q | q.NORM_K | q.FUSED_ROPE
     if not inp["producer"]:
         q.row_quantize_packed(inp["x"], packed)     # activations fixed for the whole run

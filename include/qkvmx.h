@@ -121,8 +121,10 @@ qkvmx_status rmsnorm_mx_quantize(const uint16_t* hidden, const uint16_t* residua
  * I = (num_heads + 2 * num_kv_heads) * head_dim; "Design 1)" step a).
  * ------------------------------------------------------------------------------------------ */
 
-/* Workspace bytes qkv_rowmx_project needs for its per-tile sums of squares. */
-size_t qkvmx_workspace_bytes(int64_t T, int64_t I);
+/* Workspace bytes qkv_rowmx_project needs for a [T, H] x [H, I] call: the activation codes
+ * re-laid in the kernel's LDS stage images (about T * H bytes) plus per-tile sums of squares.
+ * 0 for invalid sizes. */
+size_t qkvmx_workspace_bytes(int64_t T, int64_t H, int64_t I);
 
 /* out[t, i] = bf16_RNE( a_scale[t] * c[i] * sum_h dec(a[t, h]) * dec(W[h, i]) * 2^(E[h/32, i]-127)
  *                       + bias[i] )
@@ -135,7 +137,9 @@ size_t qkvmx_workspace_bytes(int64_t T, int64_t I);
  *   w_channel_scale  fp32 [I] per-output-channel scale ("weight_scales [1, I]"), NULL = 1.
  *   bias          bf16 [I] or NULL.
  *   layout        QKVMX_LAYOUT_BSD: out is [T, I] row-major bf16.
- *   workspace     >= qkvmx_workspace_bytes(T, I) bytes, 16-byte aligned (required iff ssq).
+ *   workspace     >= qkvmx_workspace_bytes(T, H, I) bytes, 256-byte aligned, required; its
+ *                 contents are scratch (overwritten by every call; calls sharing one workspace
+ *                 must be ordered on one stream).
  * Requires T >= 1, H % 32 == 0, head_dim % 16 == 0, num_heads >= 1, num_kv_heads >= 0,
  * a_row_stride >= H and a multiple of 4, a_codes 4-byte aligned, out 16-byte aligned. */
 qkvmx_status qkv_rowmx_project(const uint8_t* a_codes, int64_t a_row_stride,

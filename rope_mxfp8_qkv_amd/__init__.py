@@ -91,8 +91,8 @@ def rmsnorm_mx_quantize(hidden, gamma, eps: float, packed_out, residual=None, re
                                      _stream(stream)), "rmsnorm_mx_quantize")
 
 
-def qkvmx_workspace_bytes(T: int, I: int) -> int:
-    return int(lib().qkvmx_workspace_bytes(T, I))
+def qkvmx_workspace_bytes(T: int, H: int, I: int) -> int:
+    return int(lib().qkvmx_workspace_bytes(T, H, I))
 
 
 def qkv_rowmx_project(packed_a, w_packed, out, *, H: int, num_heads: int, num_kv_heads: int,

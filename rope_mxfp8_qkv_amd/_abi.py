@@ -32,7 +32,7 @@ SIGNATURES = {
     "qkv_weight_prepack": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_vp, c_sz, c_vp]),
     "row_quantize_packed": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_vp, c_vp]),
     "rmsnorm_mx_quantize": (c_i32, [c_vp, c_vp, c_vp, c_f, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp]),
-    "qkvmx_workspace_bytes": (c_sz, [c_i64, c_i64]),
+    "qkvmx_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64]),
     "qkv_rowmx_project": (c_i32, [c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_i64, c_i64, c_i32,
                                   c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "qk_norm_rope_apply": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_i32, c_i32,

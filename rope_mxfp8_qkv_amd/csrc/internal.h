@@ -12,24 +12,45 @@ namespace qkvmx {
 // Projection tile geometry (tokens x channels x K bytes per LDS stage).
 constexpr int kTileM = 256;      // tokens per block
 constexpr int kTileN = 256;      // output channels per block
-constexpr int kStageK = 128;     // K bytes per LDS stage
-constexpr int kSuperK = 256;     // K bytes per scale dword (4 MFMA steps of 64)
+constexpr int kStage = 64;       // K bytes per LDS stage (one MFMA K-step)
+constexpr int kSuperK = 256;     // K bytes per exponent dword (4 MFMA K-steps)
 constexpr int kPartialN = 128;   // channels covered by one sum-of-squares partial
+constexpr int kStageImage = kTileN * kStage;   // 16 KiB: one operand stage as stored in LDS
+constexpr int kZeroPage = 16384;               // zero bytes read in place of K past H
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Packed weight: codes [I][H] then, at a 256-byte aligned offset, the exponent dwords
-// [I][ceil(H / 256)][2].
-inline size_t packed_codes_bytes(int64_t H, int64_t I) { return (size_t)(H * I); }
-inline size_t packed_scales_offset(int64_t H, int64_t I) {
-  return (packed_codes_bytes(H, I) + 255) & ~(size_t)255;
+// Packed weight, for an [H, I] projection with NT = ceil(I / 256) channel tiles and
+// KS = 4 * ceil(H / 256) K-stages:
+//   codes   [NT][KS][16 KiB]  each block the LDS image of one stage of one channel tile
+//                             (256 rows x 64 K-bytes, 16-byte chunk c of row r stored at
+//                             chunk position c ^ ((r >> 1) & 3)); zero past I and H
+//   scales  [KS / 4][NT * 256][2] dwords: byte q of dword g of channel n in superstep s is the
+//                             E8M0 exponent of K-block 8 s + 2 q + g (127 past I / H)
+//   zero    16 KiB of zeros (read in place of activation bytes past H)
+inline int64_t packed_tiles_n(int64_t I) { return ceil_div(I, kTileN); }
+inline int64_t packed_stages(int64_t H) { return 4 * ceil_div(H, kSuperK); }
+inline size_t packed_codes_bytes(int64_t H, int64_t I) {
+  return (size_t)packed_tiles_n(I) * packed_stages(H) * kStageImage;
+}
+inline size_t packed_scales_offset(int64_t H, int64_t I) { return packed_codes_bytes(H, I); }
+inline size_t packed_scales_bytes(int64_t H, int64_t I) {
+  return (size_t)(packed_stages(H) / 4) * packed_tiles_n(I) * kTileN * 2 * 4;
+}
+inline size_t packed_zero_offset(int64_t H, int64_t I) {
+  return packed_scales_offset(H, I) + packed_scales_bytes(H, I);
 }
 inline size_t packed_total_bytes(int64_t H, int64_t I) {
-  return packed_scales_offset(H, I) + (size_t)I * (size_t)ceil_div(H, kSuperK) * 2 * 4;
+  return packed_zero_offset(H, I) + kZeroPage;
 }
 inline int64_t ssq_partials(int64_t I) { return ceil_div(I, kTileN) * (kTileN / kPartialN); }
-inline size_t workspace_total_bytes(int64_t T, int64_t I) {
-  return (size_t)ssq_partials(I) * (size_t)T * 2 * sizeof(float);
+// Projection workspace: the activation codes re-laid as stage images [MT][KS][16 KiB]
+// (MT = ceil(T / 256) token tiles), then the sum-of-squares partials [P][T][2] fp32.
+inline size_t act_image_bytes(int64_t T, int64_t H) {
+  return (size_t)ceil_div(T, kTileM) * packed_stages(H) * kStageImage;
+}
+inline size_t workspace_total_bytes(int64_t T, int64_t H, int64_t I) {
+  return act_image_bytes(T, H) + (size_t)ssq_partials(I) * (size_t)T * 2 * sizeof(float);
 }
 
 hipError_t launch_mx_weight_quantize(const float* w, int64_t H, int64_t I, uint8_t* codes,
@@ -44,7 +65,7 @@ hipError_t launch_rmsnorm_quantize(const uint16_t* hid, const uint16_t* res, con
 hipError_t launch_project(const uint8_t* a_codes, int64_t a_stride, const uint8_t* a_scales,
                           int64_t s_stride, const uint8_t* w_packed, const float* chan_scale,
                           const uint16_t* bias, int64_t T, int64_t H, int64_t I, int64_t Iq,
-                          int64_t Ik, uint16_t* out, float* ssq, float* ws, hipStream_t s);
+                          int64_t Ik, uint16_t* out, float* ssq, uint8_t* ws, hipStream_t s);
 hipError_t launch_norm_rope(uint16_t* qkv, const float* ssq, const uint16_t* q_gamma,
                             const uint16_t* k_gamma, const float* cos_tab, const float* sin_tab,
                             int64_t T, int nq, int nkv, int d, float eps, uint32_t flags,

@@ -5,22 +5,30 @@
 //
 // gfx950 design
 //  * Block tile 256 output channels x 256 tokens, 4 wavefronts (2 x 2), each 128 x 128 =
-//    4 x 4 fragments of V_MFMA_SCALE_F32_32X32X64_F8F6F4 (fp32 accumulators, 256 per lane).
+//    4 x 4 fragments of V_MFMA_SCALE_F32_32X32X64_F8F6F4 (fp32 accumulators, 256 AGPRs/lane).
 //  * Roles are swapped with respect to O = A W: the MFMA "A" operand is the weight (rows =
 //    output channels, its E8M0 block exponents feed the MFMA's A-scale directly) and the "B"
 //    operand is the ROW_MX activation (B-scale = 2^0; the fp32 row scale is applied in the
-//    epilogue).  The accumulator then holds, per lane, 4-channel runs of one token, which the
-//    epilogue stores as 8-byte bf16 vectors along the output row.
-//  * K is staged through LDS 128 bytes at a time, double-buffered (2 x (32 + 32) KiB).  Rows are
-//    stored as eight 16-byte chunks with chunk' = chunk ^ (row & 7), so the MFMA operand reads
-//    (ds_read_b128, 8 lanes = 8 consecutive rows per phase) hit 8 distinct bank groups.
+//    epilogue).  The accumulator then holds, per lane, 4-channel runs of one token.
 //  * Operand lane layout of the 32x32x64 MFMA (K = 64 bytes per row): lane group g = lane / 32
 //    holds bytes [16g, 16g + 16) and [32 + 16g, 32 + 16g + 16) of row lane % 32; the exponent
 //    of K-block b (32 bytes) of row m comes from lane m + 32 b, byte op_sel.
+//  * Operands reach LDS by direct global->LDS DMA (no staging registers), both as pre-swizzled
+//    16 KiB stage images, 1 KiB contiguous per wave instruction: the weight from its one-time
+//    prepack, the activation from a per-call repack of its rows (which are only 4-byte aligned
+//    in the packed [T, H + 4] layout, too little for 16-byte DMA).  Four LDS stage
+//    buffers (4 x 32 KiB) let each stage be requested four K-steps before it is consumed; the
+//    fragments of step s + 1 are read from LDS while the 16 MFMAs of step s run.  The DMAs are
+//    issued from inline assembly with explicit vmcnt waits, because the compiler would
+//    otherwise wait for every outstanding DMA before each LDS read.
+//  * LDS image of a stage: 256 rows x 64 K-bytes, 16-byte chunk c of row r at chunk position
+//    c ^ ((r >> 1) & 3): a ds_read_b128 phase (8 lanes = 8 consecutive rows, one logical chunk)
+//    touches 8 distinct 16-byte bank groups.
 //  * Epilogue: x = acc * a_scale[token] * c[channel] + bias[channel] in fp32, sums of x^2 per
-//    token over the Q and K columns (V excluded) written as one partial per 128 channels,
-//    then bf16 round-to-nearest-even stores.  A second small kernel adds the partials in a
-//    fixed order (deterministic, no atomics).
+//    token over the Q and K columns (V excluded) written as one partial per 128 channels, bf16
+//    round-to-nearest-even, transposed through LDS so every global store is a coalesced
+//    16-byte vector along a token row.  A small second kernel adds the partials in a fixed order
+//    (deterministic, no atomics).
 //  * Tile order: block ids are dealt round-robin to the 8 XCDs; they are remapped so that each
 //    XCD owns a contiguous range of tiles, walked in groups of 8 token tiles x all channel tiles,
 //    so the tiles resident on one XCD share activation rows and weight columns in its L2.
@@ -35,41 +43,71 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x2_a8 __attribute__((ext_vector_type(2), aligned(8)));
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 constexpr int kThreads = 256;
-constexpr int kRowBytes = kStageK;                 // 128 bytes of K per LDS row
-constexpr int kOperandBytes = kTileM * kRowBytes;  // 32 KiB per operand per stage
 constexpr int kGroupM = 8;                         // token tiles per raster group
 constexpr int kXcds = 8;
+constexpr int kBufs = 4;                           // LDS stage buffers
+constexpr int kDmaPerStage = 8;                    // per wave: 4 (weight) + 4 (activation)
+                                                   // (+ 2 exponent DMAs every 4th stage)
 
 struct ProjectArgs {
   const uint8_t* a_codes;
   int64_t a_stride;
   const uint8_t* a_scales;
   int64_t s_stride;
-  const uint8_t* w_codes;      // [I][H]
-  const uint32_t* w_scales;    // [I][S][2]
+  const uint8_t* w_img;        // [NT][KS][16 KiB]
+  const uint8_t* w_scales;     // [KS / 4][NT * 256][2] dwords
+  const uint8_t* x_img;        // activation stage images [MT][KS][16 KiB] (workspace)
   const float* chan_scale;     // [I] or null
   const uint16_t* bias;        // [I] or null
   int64_t T, H, I, Iq, Ik;
-  int64_t S;                   // supersteps of 256 K
+  int KS;                      // K-stages of 64 bytes (multiple of 4)
   int tiles_m, tiles_n;
   uint16_t* out;
   float* ws;                   // [P][T][2] or null
 };
 
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ (row & 7)) << 4);
+  return row * kStage + ((chunk ^ ((row >> 1) & 3)) << 4);
 }
 
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)(p);
+}
+
+// Global -> LDS DMA of 16 bytes per lane (lane L lands at lds + 16 L) / 4 bytes per lane.
+__device__ __forceinline__ void dma16(uint32_t lds, const void* g) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(uint32_t lds, const void* g) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(lds), "v"(g) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Instruction-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+
 __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kOperandBytes];  // [buf][W|X]
+  __shared__ __attribute__((aligned(16))) uint8_t lds_w[kBufs][kStageImage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_x[kBufs][kStageImage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sc[2][kTileN * 8];
+  // epilogue operands of this block: channel scale and bias (fp32) per channel, row scale per
+  // token; staged once so the epilogue reads them from LDS
+  __shared__ __attribute__((aligned(16))) float lds_cs[kTileN];
+  __shared__ __attribute__((aligned(16))) float lds_bias[kTileN];
+  __shared__ __attribute__((aligned(16))) float lds_sa[kTileM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in SGPRs
   const int wn = wave & 1;        // channel half of the block tile
   const int wm = wave >> 1;       // token half
 
@@ -88,58 +126,42 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   const int64_t m0 = (int64_t)tm * kTileM;
   const int64_t n0 = (int64_t)tn * kTileN;
 
-  // ---- global -> LDS assignment: thread loads chunk c of rows r0 + 32 i (i = 0..7) ----
-  // Row offsets are 32-bit (the host checks I * H and T * a_stride fit), rows past the end are
-  // clamped to the last row (their results are never stored), K past H reads as zero.
-  const int c_ld = tid & 7;
-  const int r0 = tid >> 3;
-  uint32_t woff[8], xoff[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = r0 + 32 * i;
-    const int64_t n = min(n0 + r, a.I - 1);
-    const int64_t m = min(m0 + r, a.T - 1);
-    woff[i] = (uint32_t)(n * a.H) + c_ld * 16;
-    xoff[i] = (uint32_t)(m * a.a_stride) + c_ld * 16;
+  {
+    const int64_t n = min(n0 + tid, a.I - 1);
+    lds_cs[tid] = a.chan_scale ? a.chan_scale[n] : 1.0f;
+    lds_bias[tid] = a.bias ? bf16_to_f32(a.bias[n]) : 0.0f;
+    const int64_t t = min(m0 + tid, a.T - 1);
+    lds_sa[tid] = *reinterpret_cast<const float*>(a.a_scales + t * a.s_stride);
   }
-  const int st_off = lds_off(r0, c_ld);   // + 4096 * i  (row + 32 keeps row & 7)
 
-  uint4 wreg[8], xreg[8];
-  auto gload = [&](int stage) {
-    const uint32_t k0 = (uint32_t)stage * kStageK;
-    const bool ok = (int64_t)k0 + c_ld * 16 < a.H;
+  // ---- DMA sources ----
+  // weight: wave w copies 1 KiB blocks 4 w .. 4 w + 3 of each 16 KiB stage image
+  const uint8_t* wsrc = a.w_img + ((int64_t)tn * a.KS) * kStageImage + wave * 4096 + lane * 16;
+  const uint32_t wdst = lds_addr(&lds_w[0][0]) + wave * 4096;
+  // exponents: each wave copies 512 bytes (two dword DMAs) of the 2 KiB per superstep
+  const uint8_t* ssrc = a.w_scales + ((int64_t)tn * kTileN * 2) * 4 + wave * 512 + lane * 4;
+  const int64_t s_step = (int64_t)a.tiles_n * kTileN * 2 * 4;       // bytes per superstep
+  const uint32_t sdst = lds_addr(&lds_sc[0][0]) + wave * 512;
+  // activation: same scheme as the weight, from the per-call stage images
+  const uint8_t* xsrc = a.x_img + ((int64_t)tm * a.KS) * kStageImage + wave * 4096 + lane * 16;
+  const uint32_t xdst = lds_addr(&lds_x[0][0]) + wave * 4096;
+
+  // DMA of stage t (t % 4 == Q) into buffer Q; a stage opening a superstep also brings that
+  // superstep's exponents into ring slot (t / 4) % 2.
+  auto issue = [&](auto q_c, int t) {
+    constexpr int Q = decltype(q_c)::value;
+    if (Q == 0) {
+      const int64_t sup = t >> 2;
+      const uint32_t slot = sdst + (uint32_t)(sup & 1) * 2048;
+      dma4(slot, ssrc + sup * s_step);
+      dma4(slot + 256, ssrc + sup * s_step + 256);
+    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (ok) {
-        wreg[i] = *reinterpret_cast<const uint4*>(a.w_codes + (woff[i] + k0));
-        const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(a.a_codes + (xoff[i] + k0));
-        xreg[i] = make_uint4(v.x, v.y, v.z, v.w);
-      } else {
-        wreg[i] = make_uint4(0, 0, 0, 0);
-        xreg[i] = make_uint4(0, 0, 0, 0);
-      }
+    for (int i = 0; i < 4; ++i) {
+      dma16(wdst + Q * kStageImage + i * 1024, wsrc + (int64_t)t * kStageImage + i * 1024);
+      dma16(xdst + Q * kStageImage + i * 1024, xsrc + (int64_t)t * kStageImage + i * 1024);
     }
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<uint4*>(&lds[buf][0][st_off + 4096 * i]) = wreg[i];
-      *reinterpret_cast<uint4*>(&lds[buf][1][st_off + 4096 * i]) = xreg[i];
-    }
-  };
-
-  // ---- per-lane exponent dwords for the 4 channel fragments ----
-  const int g = lane >> 5;
-  const uint32_t* scp[4];
-#pragma unroll
-  for (int cf = 0; cf < 4; ++cf) {
-    int64_t n = n0 + wn * 128 + cf * 32 + (lane & 31);
-    n = n < a.I ? n : a.I - 1;
-    scp[cf] = a.w_scales + n * a.S * 2 + g;
-  }
-  uint32_t sc_cur[4], sc_nxt[4];
-#pragma unroll
-  for (int cf = 0; cf < 4; ++cf) sc_cur[cf] = scp[cf][0];
 
   v16f acc[4][4];
 #pragma unroll
@@ -149,113 +171,138 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[cf][tf][r] = 0.0f;
 
+  const int g = lane >> 5;
   const int fr = lane & 31;           // fragment row of this lane
   const int w_row0 = wn * 128 + fr;   // + 32 cf
   const int x_row0 = wm * 128 + fr;   // + 32 tf
+  // the two 16-byte halves a lane feeds to the MFMA: chunks g and 2 + g of its row; rows
+  // 32 f apart share the swizzle, so fragment f sits 32 * 64 * f bytes further on
+  const int rw0 = lds_off(w_row0, g), rw1 = lds_off(w_row0, 2 + g);
+  const int rx0 = lds_off(x_row0, g), rx1 = lds_off(x_row0, 2 + g);
+  const int rsc = (w_row0 * 2 + g) * 4;   // + 32 * 8 cf: this lane's exponent dword
 
-  // One LDS stage = 2 MFMA K-steps (kk); exponent byte = 2 * st + kk.
-  auto compute = [&](auto st_c) {
-    constexpr int st = decltype(st_c)::value;
+  v8i wf[2][4], xf[2][4];
+  uint32_t sc[2][4];
+  auto fload = [&](int buf, v8i (&wd)[4], v8i (&xd)[4]) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      v8i wf[4], xf[4];
-      const int c0 = 4 * kk + g, c1 = 4 * kk + 2 + g;
-#pragma unroll
-      for (int cf = 0; cf < 4; ++cf) {
-        const int r = w_row0 + 32 * cf;
-        const uint4 p0 = *reinterpret_cast<const uint4*>(&lds[st][0][lds_off(r, c0)]);
-        const uint4 p1 = *reinterpret_cast<const uint4*>(&lds[st][0][lds_off(r, c1)]);
-        wf[cf] = v8i{(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w,
-                     (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
-      }
-#pragma unroll
-      for (int tf = 0; tf < 4; ++tf) {
-        const int r = x_row0 + 32 * tf;
-        const uint4 p0 = *reinterpret_cast<const uint4*>(&lds[st][1][lds_off(r, c0)]);
-        const uint4 p1 = *reinterpret_cast<const uint4*>(&lds[st][1][lds_off(r, c1)]);
-        xf[tf] = v8i{(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w,
-                     (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
-      }
-#pragma unroll
-      for (int cf = 0; cf < 4; ++cf)
-#pragma unroll
-        for (int tf = 0; tf < 4; ++tf) {
-          if (kk == 0)
-            acc[cf][tf] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                wf[cf], xf[tf], acc[cf][tf], 0, 0, 2 * st, (int)sc_cur[cf], 0, 0x7F7F7F7F);
-          else
-            acc[cf][tf] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                wf[cf], xf[tf], acc[cf][tf], 0, 0, 2 * st + 1, (int)sc_cur[cf], 0, 0x7F7F7F7F);
-        }
+    for (int f = 0; f < 4; ++f) {
+      const uint4 p0 = *reinterpret_cast<const uint4*>(&lds_w[buf][rw0 + 2048 * f]);
+      const uint4 p1 = *reinterpret_cast<const uint4*>(&lds_w[buf][rw1 + 2048 * f]);
+      wd[f] = v8i{(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w,
+                  (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
+      const uint4 q0 = *reinterpret_cast<const uint4*>(&lds_x[buf][rx0 + 2048 * f]);
+      const uint4 q1 = *reinterpret_cast<const uint4*>(&lds_x[buf][rx1 + 2048 * f]);
+      xd[f] = v8i{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w,
+                  (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
     }
   };
+  auto sload = [&](int slot, uint32_t (&sd)[4]) {
+#pragma unroll
+    for (int cf = 0; cf < 4; ++cf)
+      sd[cf] = *reinterpret_cast<const uint32_t*>(&lds_sc[slot][rsc + 256 * cf]);
+  };
 
-  // ---- main loop over 256-K supersteps (2 LDS stages each) ----
-  const int nstages = (int)(2 * a.S);
-  gload(0);
-  lstore(0);
+  // ---- software pipeline over K-steps of 64 bytes ----
+  // Step s: fragments of stage s are in registers [s & 1]; the step issues its 16 MFMAs
+  // while reading stage s + 1's fragments (and, on the last step of a superstep, the next
+  // superstep's exponents) and DMA-ing stage s + 4 into the buffer stage s occupied.  It ends
+  // by waiting for its own DMA of stage s + 2 (the most recent DMA groups, of stages s + 3 and
+  // s + 4, may stay in flight) and a barrier, after which stage s + 2 is complete in LDS for
+  // all waves and every wave has finished reading stage s + 1's buffer predecessor.
+  const int KS = a.KS;
+  issue(std::integral_constant<int, 0>{}, 0);
+  issue(std::integral_constant<int, 1>{}, 1);
+  issue(std::integral_constant<int, 2>{}, 2);
+  issue(std::integral_constant<int, 3>{}, 3);
+  wait_vm<3 * kDmaPerStage>();
   __syncthreads();
-  for (int64_t s = 0; s < a.S; ++s) {
-    // stage 2s (buffer 0)
-    if (2 * s + 1 < nstages) gload((int)(2 * s + 1));
-    if (s + 1 < a.S) {
+  fload(0, wf[0], xf[0]);
+  sload(0, sc[0]);
+  wait_vm<2 * kDmaPerStage>();
+  __syncthreads();
+
+  auto step = [&](auto q_c, int s, auto issue_c, auto wait_c) {
+    constexpr int q = decltype(q_c)::value;        // step within the 256-K superstep
+    constexpr int p = q & 1;
+    constexpr int sp = (q == 3) ? 1 : 0;           // exponent set of the next step
+    constexpr bool do_issue = decltype(issue_c)::value;
+    constexpr int nwait = decltype(wait_c)::value;
+    const int ssup = s >> 2;
+    fload((s + 1) & (kBufs - 1), wf[p ^ 1], xf[p ^ 1]);
+    if (q == 3) sload((ssup + 1) & 1, sc[1]);
 #pragma unroll
-      for (int cf = 0; cf < 4; ++cf) sc_nxt[cf] = scp[cf][(s + 1) * 2];
-    }
-    compute(std::integral_constant<int, 0>{});
-    if (2 * s + 1 < nstages) lstore(1);
-    __syncthreads();
-    // stage 2s + 1 (buffer 1)
-    if (2 * s + 2 < nstages) gload((int)(2 * s + 2));
-    compute(std::integral_constant<int, 1>{});
-    if (2 * s + 2 < nstages) lstore(0);
-    __syncthreads();
-    if (s + 1 < a.S) {
+    for (int cf = 0; cf < 4; ++cf)
 #pragma unroll
-      for (int cf = 0; cf < 4; ++cf) sc_cur[cf] = sc_nxt[cf];
+      for (int tf = 0; tf < 4; ++tf)
+        acc[cf][tf] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            wf[p][cf], xf[p][tf], acc[cf][tf], 0, 0, q, (int)sc[0][cf], 0, 0x7F7F7F7F);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
+    if (do_issue) issue(q_c, s + 4);
+    if (q == 3) {
+#pragma unroll
+      for (int cf = 0; cf < 4; ++cf) sc[0][cf] = sc[1][cf];
+    }
+    (void)sp;
+    if (nwait >= 0) wait_vm<(nwait < 0 ? 0 : nwait)>();
+    __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using Yes = std::true_type;
+  using No = std::false_type;
+  using W40 = std::integral_constant<int, 2 * kDmaPerStage>;
+  using W20 = std::integral_constant<int, kDmaPerStage>;
+  using W0 = std::integral_constant<int, 0>;
+  using WN = std::integral_constant<int, -1>;
+  for (int s = 0; s < KS - 4; s += 4) {
+    step(I0{}, s, Yes{}, W40{});
+    step(I1{}, s + 1, Yes{}, W40{});
+    step(I2{}, s + 2, Yes{}, W40{});
+    step(I3{}, s + 3, Yes{}, W40{});
   }
+  // last superstep: nothing left to request; the waits shrink with the groups in flight
+  step(I0{}, KS - 4, No{}, W20{});
+  step(I1{}, KS - 3, No{}, W0{});
+  step(I2{}, KS - 2, No{}, WN{});
+  step(I3{}, KS - 1, No{}, WN{});
 
   // ---- epilogue ----
-  float sA[4];
-  int64_t tok[4];
-#pragma unroll
-  for (int tf = 0; tf < 4; ++tf) {
-    tok[tf] = m0 + wm * 128 + tf * 32 + fr;
-    const int64_t t = tok[tf] < a.T ? tok[tf] : a.T - 1;
-    sA[tf] = *reinterpret_cast<const float*>(a.a_scales + t * a.s_stride);
-  }
+  // x = acc * a_scale * c + bias (fp32) -> sums of squares from the fp32 values, bf16 into a
+  // per-wave 128 x 128 LDS tile (token rows of 256 bytes, 16-byte chunk j of row r at chunk
+  // position j ^ (r & 15)), then read back row-contiguous and stored as 16-byte vectors.
+  __builtin_amdgcn_sched_barrier(0);
+  uint8_t* const otile = (wm == 0 ? &lds_w[0][0] : &lds_x[0][0]) + wn * 32768;
   float sq_q[4] = {0.f, 0.f, 0.f, 0.f}, sq_k[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int cf = 0; cf < 4; ++cf) {
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
-      const int64_t n = n0 + wn * 128 + cf * 32 + rq * 8 + g * 4;   // 4 consecutive channels
-      if (n >= a.I) continue;
-      float cs[4] = {1.f, 1.f, 1.f, 1.f}, bs[4] = {0.f, 0.f, 0.f, 0.f};
-      if (a.chan_scale) {
-        const float4 v = *reinterpret_cast<const float4*>(a.chan_scale + n);
-        cs[0] = v.x; cs[1] = v.y; cs[2] = v.z; cs[3] = v.w;
-      }
-      if (a.bias) {
-        const u32x2_a8 v = *reinterpret_cast<const u32x2_a8*>(a.bias + n);
-        bs[0] = bf16_to_f32(v.x & 0xFFFFu); bs[1] = bf16_to_f32(v.x >> 16);
-        bs[2] = bf16_to_f32(v.y & 0xFFFFu); bs[3] = bf16_to_f32(v.y >> 16);
-      }
-      const bool in_q = n < a.Iq;
-      const bool in_k = !in_q && n < a.Iq + a.Ik;
+      const int cl = cf * 32 + rq * 8 + g * 4;            // 4 consecutive channels (local)
+      const float4 c4 = *reinterpret_cast<const float4*>(&lds_cs[wn * 128 + cl]);
+      const float4 b4 = *reinterpret_cast<const float4*>(&lds_bias[wn * 128 + cl]);
+      const float cs[4] = {c4.x, c4.y, c4.z, c4.w}, bs[4] = {b4.x, b4.y, b4.z, b4.w};
+      const int64_t ng = n0 + wn * 128 + cl;
+      const bool in_q = ng < a.Iq;
+      const bool in_k = !in_q && ng < a.Iq + a.Ik;
 #pragma unroll
       for (int tf = 0; tf < 4; ++tf) {
+        const float sa = lds_sa[wm * 128 + tf * 32 + fr];
         float x[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = acc[cf][tf][rq * 4 + e] * sA[tf] * cs[e] + bs[e];
+        for (int e = 0; e < 4; ++e) x[e] = acc[cf][tf][rq * 4 + e] * sa * cs[e] + bs[e];
         const float s2 = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
         if (in_q) sq_q[tf] += s2;
         if (in_k) sq_k[tf] += s2;
-        if (tok[tf] < a.T) {
-          u32x2_a8 o = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-          *reinterpret_cast<u32x2_a8*>(a.out + tok[tf] * a.I + n) = o;
-        }
+        const int row = tf * 32 + fr;
+        const int chunk = cf * 4 + rq;
+        u32x2_a8 o = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+        *reinterpret_cast<u32x2_a8*>(otile + row * 256 + ((chunk ^ (row & 15)) << 4) + g * 8) = o;
       }
     }
   }
@@ -265,12 +312,46 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     for (int tf = 0; tf < 4; ++tf) {
       const float q = sq_q[tf] + __shfl_xor(sq_q[tf], 32);
       const float k = sq_k[tf] + __shfl_xor(sq_k[tf], 32);
-      if (g == 0 && tok[tf] < a.T) {
+      const int64_t tok = m0 + wm * 128 + tf * 32 + fr;
+      if (g == 0 && tok < a.T) {
         u32x2_a8 o = {__float_as_uint(q), __float_as_uint(k)};
-        *reinterpret_cast<u32x2_a8*>(a.ws + (p * a.T + tok[tf]) * 2) = o;
+        *reinterpret_cast<u32x2_a8*>(a.ws + (p * a.T + tok) * 2) = o;
       }
     }
   }
+  // row-contiguous read-back: 16 lanes per 256-byte token row, 4 rows per instruction
+  const int jc = lane & 15;
+  const int64_t ch = n0 + wn * 128 + jc * 8;
+  const bool ch_ok = ch < a.I;
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int row = it * 4 + (lane >> 4);
+    const uint4 v = *reinterpret_cast<const uint4*>(otile + row * 256 + ((jc ^ (row & 15)) << 4));
+    const int64_t tok = m0 + wm * 128 + row;
+    if (ch_ok && tok < a.T) *reinterpret_cast<uint4*>(a.out + tok * a.I + ch) = v;
+  }
+}
+
+// Activation codes [T, stride] (rows only 4-byte aligned in the packed [T, H + 4] layout) ->
+// the stage images the projection DMA-copies: per (token tile tm, K-stage t) 256 rows x 64
+// bytes with 16-byte chunk c of row r at chunk position c ^ ((r >> 1) & 3); zero past T or H.
+// One thread per 16-byte position.
+__global__ void __launch_bounds__(256) act_repack_kernel(const uint8_t* __restrict__ a,
+                                                         int64_t stride, int64_t T, int64_t H,
+                                                         int KS, uint8_t* __restrict__ img) {
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;   // 0..1023
+  const int64_t t = blockIdx.y;
+  const int64_t tm = blockIdx.z;
+  const int r = p >> 2;
+  const int c = (p & 3) ^ ((r >> 1) & 3);
+  const int64_t m = tm * kTileM + r;
+  const int64_t k = t * kStage + 16 * c;
+  uint4 o = make_uint4(0, 0, 0, 0);
+  if (m < T && k < H) {
+    const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(a + m * stride + k);
+    o = make_uint4(v.x, v.y, v.z, v.w);
+  }
+  reinterpret_cast<uint4*>(img)[(tm * KS + t) * (kStageImage / 16) + p] = o;
 }
 
 // ssq[t] = sum over partials p of ws[p][t] (fixed order).
@@ -292,25 +373,31 @@ __global__ void __launch_bounds__(256) ssq_reduce_kernel(const float* __restrict
 hipError_t launch_project(const uint8_t* a_codes, int64_t a_stride, const uint8_t* a_scales,
                           int64_t s_stride, const uint8_t* w_packed, const float* chan_scale,
                           const uint16_t* bias, int64_t T, int64_t H, int64_t I, int64_t Iq,
-                          int64_t Ik, uint16_t* out, float* ssq, float* ws, hipStream_t s) {
+                          int64_t Ik, uint16_t* out, float* ssq, uint8_t* ws, hipStream_t s) {
   ProjectArgs a;
   a.a_codes = a_codes; a.a_stride = a_stride; a.a_scales = a_scales; a.s_stride = s_stride;
-  a.w_codes = w_packed;
-  a.w_scales = reinterpret_cast<const uint32_t*>(w_packed + packed_scales_offset(H, I));
+  a.w_img = w_packed;
+  a.w_scales = w_packed + packed_scales_offset(H, I);
+  a.x_img = ws;
   a.chan_scale = chan_scale; a.bias = bias;
   a.T = T; a.H = H; a.I = I; a.Iq = Iq; a.Ik = Ik;
-  a.S = ceil_div(H, kSuperK);
+  a.KS = (int)packed_stages(H);
   a.tiles_m = (int)ceil_div(T, kTileM);
-  a.tiles_n = (int)ceil_div(I, kTileN);
+  a.tiles_n = (int)packed_tiles_n(I);
   a.out = out;
-  a.ws = ssq ? ws : nullptr;
+  float* partials = reinterpret_cast<float*>(ws + act_image_bytes(T, H));
+  a.ws = ssq ? partials : nullptr;
+  dim3 rg(kStageImage / 16 / 256, (unsigned)a.KS, (unsigned)a.tiles_m);
+  hipLaunchKernelGGL(act_repack_kernel, rg, dim3(256), 0, s, a_codes, a_stride, T, H, a.KS, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const unsigned nblocks = (unsigned)(a.tiles_m * a.tiles_n);
   hipLaunchKernelGGL(project_kernel, dim3(nblocks), dim3(kThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess || !ssq) return e;
   const int64_t P = ssq_partials(I);
-  hipLaunchKernelGGL(ssq_reduce_kernel, dim3((unsigned)ceil_div(T, 256)), dim3(256), 0, s, ws, P,
-                     T, ssq);
+  hipLaunchKernelGGL(ssq_reduce_kernel, dim3((unsigned)ceil_div(T, 256)), dim3(256), 0, s,
+                     partials, P, T, ssq);
   return hipGetLastError();
 }
 

@@ -74,7 +74,6 @@ qkvmx_status qkv_weight_prepack(const uint8_t* w_h4_i_4, const uint8_t* w_e8m0, 
                                 hipStream_t stream) {
   if (!w_h4_i_4 || !w_e8m0 || !w_packed) return fail(QKVMX_ERR_NULL, "qkv_weight_prepack: null pointer");
   if (H <= 0 || I <= 0 || H % 32) return fail(QKVMX_ERR_SHAPE, "qkv_weight_prepack: need H %% 32 == 0, H, I > 0");
-  if (H * I >= kMaxOffset) return fail(QKVMX_ERR_UNSUPPORTED, "qkv_weight_prepack: H * I must be < 2^31");
   if (w_packed_bytes < packed_total_bytes(H, I))
     return fail(QKVMX_ERR_SHAPE, "qkv_weight_prepack: w_packed_bytes %zu < %zu", w_packed_bytes, packed_total_bytes(H, I));
   if (!aligned(w_h4_i_4, 4) || !aligned(w_packed, 256)) return fail(QKVMX_ERR_ALIGN, "qkv_weight_prepack: codes 4-byte, w_packed 256-byte aligned");
@@ -110,9 +109,9 @@ qkvmx_status rmsnorm_mx_quantize(const uint16_t* hidden, const uint16_t* residua
                                             packed_out, stream), "rmsnorm_mx_quantize");
 }
 
-size_t qkvmx_workspace_bytes(int64_t T, int64_t I) {
-  if (T <= 0 || I <= 0) return 0;
-  return workspace_total_bytes(T, I);
+size_t qkvmx_workspace_bytes(int64_t T, int64_t H, int64_t I) {
+  if (T <= 0 || H <= 0 || I <= 0 || H % 32) return 0;
+  return workspace_total_bytes(T, H, I);
 }
 
 qkvmx_status qkv_rowmx_project(const uint8_t* a_codes, int64_t a_row_stride,
@@ -123,7 +122,7 @@ qkvmx_status qkv_rowmx_project(const uint8_t* a_codes, int64_t a_row_stride,
                                uint16_t* out, float* ssq, void* workspace, size_t ws_bytes,
                                hipStream_t stream) {
   if (!a_codes || !a_scales || !w_packed || !out) return fail(QKVMX_ERR_NULL, "qkv_rowmx_project: null pointer");
-  if (ssq && !workspace) return fail(QKVMX_ERR_WORKSPACE, "qkv_rowmx_project: ssq requested without a workspace");
+  if (!workspace) return fail(QKVMX_ERR_WORKSPACE, "qkv_rowmx_project: workspace is required");
   if (T <= 0 || H <= 0 || H % 32) return fail(QKVMX_ERR_SHAPE, "qkv_rowmx_project: need T > 0, H %% 32 == 0");
   if (num_heads < 1 || num_kv_heads < 0 || head_dim <= 0 || head_dim % 16)
     return fail(QKVMX_ERR_SHAPE, "qkv_rowmx_project: need num_heads >= 1, num_kv_heads >= 0, head_dim %% 16 == 0");
@@ -131,18 +130,18 @@ qkvmx_status qkv_rowmx_project(const uint8_t* a_codes, int64_t a_row_stride,
   if (a_row_stride < H || a_row_stride % 4 || a_scale_stride <= 0 || a_scale_stride % 4)
     return fail(QKVMX_ERR_SHAPE, "qkv_rowmx_project: a_row_stride >= H and strides multiples of 4");
   const int64_t I = (int64_t)(num_heads + 2 * (int64_t)num_kv_heads) * head_dim;
-  if (H * I >= kMaxOffset || (T - 1) * a_row_stride + H >= kMaxOffset)
-    return fail(QKVMX_ERR_UNSUPPORTED, "qkv_rowmx_project: weight or activation span must be < 2^31 bytes");
-  if (ssq && ws_bytes < workspace_total_bytes(T, I))
-    return fail(QKVMX_ERR_WORKSPACE, "qkv_rowmx_project: workspace %zu < %zu bytes", ws_bytes, workspace_total_bytes(T, I));
+  if ((T - 1) * a_row_stride + H >= kMaxOffset)
+    return fail(QKVMX_ERR_UNSUPPORTED, "qkv_rowmx_project: activation span must be < 2^31 bytes");
+  if (ws_bytes < workspace_total_bytes(T, H, I))
+    return fail(QKVMX_ERR_WORKSPACE, "qkv_rowmx_project: workspace %zu < %zu bytes", ws_bytes, workspace_total_bytes(T, H, I));
   if (!aligned(a_codes, 4) || !aligned(a_scales, 4) || !aligned(w_packed, 256) ||
       (w_channel_scale && !aligned(w_channel_scale, 16)) || (bias && !aligned(bias, 8)) ||
-      !aligned(out, 16) || (ssq && (!aligned(ssq, 8) || !aligned(workspace, 16))))
-    return fail(QKVMX_ERR_ALIGN, "qkv_rowmx_project: alignment (codes/scales 4, w_packed 256, channel scale 16, bias 8, out 16, ssq 8, workspace 16)");
+      !aligned(out, 16) || (ssq && !aligned(ssq, 8)) || !aligned(workspace, 256))
+    return fail(QKVMX_ERR_ALIGN, "qkv_rowmx_project: alignment (codes/scales 4, w_packed 256, channel scale 16, bias 8, out 16, ssq 8, workspace 256)");
   const int64_t Iq = (int64_t)num_heads * head_dim, Ik = (int64_t)num_kv_heads * head_dim;
   return hip_status(launch_project(a_codes, a_row_stride, a_scales, a_scale_stride,
                                    (const uint8_t*)w_packed, w_channel_scale, bias, T, H, I, Iq,
-                                   Ik, out, ssq, (float*)workspace, stream), "qkv_rowmx_project");
+                                   Ik, out, ssq, (uint8_t*)workspace, stream), "qkv_rowmx_project");
 }
 
 qkvmx_status qk_norm_rope_apply(uint16_t* qkv, const float* ssq, const uint16_t* q_gamma,

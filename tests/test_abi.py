@@ -48,8 +48,10 @@ def test_size_queries():
     L = _lib()
     assert L.qkv_weight_packed_bytes(5120, 15360) >= 5120 * 15360 + 15360 * 20 * 8
     assert L.qkv_weight_packed_bytes(100, 16) == 0           # H % 32 != 0
-    assert L.qkvmx_workspace_bytes(75600, 15360) == 120 * 75600 * 8
-    assert L.qkvmx_workspace_bytes(0, 16) == 0
+    # activation stage images (296 token tiles x 80 stages x 16 KiB) + 120 partials per token
+    assert L.qkvmx_workspace_bytes(75600, 5120, 15360) == 296 * 80 * 16384 + 120 * 75600 * 8
+    assert L.qkvmx_workspace_bytes(0, 256, 16) == 0
+    assert L.qkvmx_workspace_bytes(4, 100, 16) == 0
 
 
 P = 0x10000   # a fake, well-aligned device address: validation fails before it is used
@@ -58,7 +60,7 @@ P = 0x10000   # a fake, well-aligned device address: validation fails before it 
 def _proj(L, **kw):
     a = dict(a_codes=P, a_row_stride=260, a_scales=P + 256, a_scale_stride=260, w_packed=P,
              w_channel_scale=None, bias=None, T=4, H=256, num_heads=2, num_kv_heads=2,
-             head_dim=64, layout=0, out=P, ssq=None, workspace=None, ws_bytes=0, stream=None)
+             head_dim=64, layout=0, out=P, ssq=None, workspace=P, ws_bytes=1 << 30, stream=None)
     a.update(kw)
     return L.qkv_rowmx_project(*a.values())
 
@@ -79,8 +81,9 @@ def test_projection_validation():
     assert _proj(L, T=0) == 2
     assert _proj(L, layout=1) == 6
     assert _proj(L, a_row_stride=258) == 2
-    assert _proj(L, ssq=P) == 5                                   # ssq without workspace
+    assert _proj(L, workspace=None) == 5                          # workspace is required
     assert _proj(L, ssq=P, workspace=P, ws_bytes=8) == 5          # workspace too small
+    assert _proj(L, workspace=P + 16) == 3
     assert _proj(L, out=P + 2) == 3
     assert _proj(L, a_scales=P + 2) == 3
     assert _proj(L, w_packed=P + 16) == 3

@@ -110,12 +110,12 @@ def run_projection(q, inp: G.ProjInputs, dev, chan_scale=None, with_ssq=True):
     wp = q.prepare_weight(G.to_dev(inp.w_codes, dev), G.to_dev(inp.w_e8m0, dev), p.H, p.I)
     out = torch.full((p.T, p.I), float("nan"), dtype=torch.bfloat16, device=dev)
     ssq = torch.full((p.T, 2), float("nan"), dtype=torch.float32, device=dev) if with_ssq else None
-    ws = torch.empty(q.qkvmx_workspace_bytes(p.T, p.I), dtype=torch.uint8, device=dev)
+    ws = torch.empty(q.qkvmx_workspace_bytes(p.T, p.H, p.I), dtype=torch.uint8, device=dev)
     q.qkv_rowmx_project(G.to_dev(inp.packed, dev), wp, out, H=p.H, num_heads=p.num_heads,
                         num_kv_heads=p.num_kv_heads, head_dim=p.head_dim,
                         channel_scale=None if chan_scale is None else G.to_dev(chan_scale, dev),
                         bias=None if inp.bias is None else G.bf16_dev(inp.bias, dev), ssq=ssq,
-                        workspace=ws if with_ssq else None)
+                        workspace=ws)
     return out, ssq, wp
 
 
@@ -149,9 +149,10 @@ def test_projection_separate_scale_buffer_and_no_bias():
                           num_kv_heads=1, head_dim=64)
     wp = q.prepare_weight(G.to_dev(inp.w_codes, dev), G.to_dev(inp.w_e8m0, dev), p.H, p.I)
     out = torch.empty((p.T, p.I), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(q.qkvmx_workspace_bytes(p.T, p.H, p.I), dtype=torch.uint8, device=dev)
     q.qkv_rowmx_project(G.to_dev(np.ascontiguousarray(codes), dev), wp, out, H=p.H, num_heads=2,
                         num_kv_heads=1, head_dim=64, a_scales=G.to_dev(sA, dev), a_row_stride=p.H,
-                        a_scale_stride=4)
+                        a_scale_stride=4, workspace=ws)
     torch.cuda.synchronize()
     G.check_close(G.bf16_host(out), X, "separate-scale X")
 
