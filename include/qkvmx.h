@@ -167,7 +167,8 @@ qkvmx_status qkv_rowmx_project(const uint8_t* a_codes, int64_t a_row_stride,
  *   k_gamma   bf16 [num_kv_heads * d]; required iff QKVMX_NORM_K, must be NULL otherwise.
  *   cos_tab, sin_tab  fp32 [T, d] rotate-half caches; required iff QKVMX_FUSED_ROPE.
  * num_kv_heads == 0 is a single-segment call: QKVMX_NORM_K is then an error.
- * Requires head_dim % 16 == 0; qkv 16-byte aligned; tables and ssq 16-byte aligned. */
+ * Requires head_dim % 16 == 0 and head_dim <= 1024; qkv, gamma and the tables 16-byte aligned,
+ * ssq 8-byte aligned. */
 qkvmx_status qk_norm_rope_apply(uint16_t* qkv, const float* ssq, const uint16_t* q_gamma,
                                 const uint16_t* k_gamma, const float* cos_tab,
                                 const float* sin_tab, int64_t T, int32_t num_heads,

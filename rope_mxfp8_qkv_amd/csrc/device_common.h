@@ -28,18 +28,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 //    smallest normal, 0x08, so the carry into the exponent field is automatic).
 //  - otherwise round the fp32 mantissa to 3 bits (RNE on the bit pattern) and rebias the
 //    exponent from 127 to 7; a mantissa carry moves into the exponent field by itself.
+// Both candidates are computed and one is selected, so the conversion is branch-free.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
-  uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  float a = fminf(fabsf(v), 448.0f);
-  uint32_t code;
-  if (a < 0.015625f) {
-    code = (uint32_t)rintf(a * 512.0f);
-  } else {
-    uint32_t b = __float_as_uint(a);
-    b += 0x7FFFFu + ((b >> 20) & 1u);
-    code = (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);
-  }
-  return code | sign;
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fminf(fabsf(v), 448.0f);
+  const uint32_t sub = (uint32_t)rintf(a * 512.0f);
+  uint32_t b = __float_as_uint(a);
+  b += 0x7FFFFu + ((b >> 20) & 1u);
+  const uint32_t nrm = (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);
+  return (a < 0.015625f ? sub : nrm) | sign;
 }
 
 }  // namespace qkvmx

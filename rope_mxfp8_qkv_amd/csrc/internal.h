@@ -20,11 +20,16 @@ constexpr int kZeroPage = 16384;               // zero bytes read in place of K 
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Chunk swizzle of a stage image row (four 16-byte chunks of K per 64-byte row).  Rows r and
+// r + 4 k (k = 1, 2, 3) get distinct values, and so do rows r and r + 2 k: the 16 rows one
+// ds_read_b128 serves fall into 16 distinct 16-byte bank groups of a 256-byte LDS window.
+__host__ __device__ inline int stage_swizzle(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+
 // Packed weight, for an [H, I] projection with NT = ceil(I / 256) channel tiles and
 // KS = 4 * ceil(H / 256) K-stages:
 //   codes   [NT][KS][16 KiB]  each block the LDS image of one stage of one channel tile
 //                             (256 rows x 64 K-bytes, 16-byte chunk c of row r stored at
-//                             chunk position c ^ ((r >> 1) & 3)); zero past I and H
+//                             chunk position c ^ stage_swizzle(r)); zero past I and H
 //   scales  [KS / 4][NT * 256][2] dwords: byte q of dword g of channel n in superstep s is the
 //                             E8M0 exponent of K-block 8 s + 2 q + g (127 past I / H)
 //   zero    16 KiB of zeros (read in place of activation bytes past H)

@@ -3,16 +3,24 @@
 // never read or written.  HBM-bound: per token 4 * (Iq + Ik) bytes of Q/K plus the token's
 // cos/sin rows (8 * d bytes) and its two sums; gamma is shared by all tokens and stays cached.
 //
-// Work unit = (segment, head, 8-lane chunk j0): the thread loads lanes j0..j0+7 and their
-// rotate-half partners j0+d/2.. as two 16-byte vectors, so the 8 threads of a head read
-// 2 x 128 contiguous bytes for d = 128.  The per-token inv_rms is computed once per thread
-// from the token's sums and folded into the gamma multiply, as the pages fold it into cos/sin.
+// Thread layout: 64 threads per token; thread (j, hg) owns the 8-lane chunk j0 = 8 j of every
+// head h = hg, hg + G, hg + 2 G, ... (G = 64 / (d / 16) head groups) together with the chunk's
+// rotate-half partners j0 + d/2 .. j0 + d/2 + 7.  The token's cos/sin values for those 16 lanes
+// and its inv_rms are loaded once per thread and reused for every head, as the pages broadcast
+// the position-only tables across heads; each head costs two independent 16-byte loads of x
+// (plus gamma, an L1/L2 hit) and two 16-byte streaming stores.  The 8 threads of a head read
+// 2 x 128 contiguous bytes (d = 128).  inv_rms is folded into the gamma multiply.
 #include "device_common.h"
 #include "internal.h"
 
 namespace qkvmx {
 
 namespace {
+
+constexpr int kThreadsPerToken = 64;
+constexpr int kTokensPerBlock = 4;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct NormRopeArgs {
   uint16_t* qkv;
@@ -24,9 +32,8 @@ struct NormRopeArgs {
   int64_t T;
   int64_t I;
   int nq, nkv, d;
-  int units_q;       // active Q units per token (0 if the Q segment is untouched)
-  int units;         // active units per token
-  int blocks_per_token;
+  int heads_q;       // heads of the Q segment that are touched (0 if Q is untouched)
+  int heads;         // touched heads in total (Q heads first, then K heads)
   float eps;
   bool norm_q, norm_k, rope;
 };
@@ -40,9 +47,9 @@ __device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
   }
 }
 
-__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
-  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                    pack_bf16x2(f[6], f[7]));
+__device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
+  return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+               pack_bf16x2(f[6], f[7])};
 }
 
 __device__ __forceinline__ void load8f(const float* p, float (&f)[8]) {
@@ -52,56 +59,67 @@ __device__ __forceinline__ void load8f(const float* p, float (&f)[8]) {
   f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
-__global__ void __launch_bounds__(1024) norm_rope_kernel(const NormRopeArgs a) {
-  const int64_t token = blockIdx.x / a.blocks_per_token;
-  const int u = (blockIdx.x % a.blocks_per_token) * blockDim.x + threadIdx.x;
-  if (u >= a.units) return;
-  const int cpd = a.d / 16;                 // chunks per head
-  const bool is_k = u >= a.units_q;
-  const int uu = is_k ? u - a.units_q : u;
-  const int head = uu / cpd;
-  const int j0 = (uu % cpd) * 8;
+__global__ void __launch_bounds__(kThreadsPerToken * kTokensPerBlock) norm_rope_kernel(
+    const NormRopeArgs a) {
+  const int64_t token = (int64_t)blockIdx.x * kTokensPerBlock + (threadIdx.x / kThreadsPerToken);
+  if (token >= a.T) return;
+  const int lane = threadIdx.x % kThreadsPerToken;
+  const int cpd = a.d / 16;                 // chunks per head half-pair
+  const int ngroups = kThreadsPerToken / cpd;
+  const int j0 = (lane % cpd) * 8;
+  const int hg = lane / cpd;
   const int half = a.d / 2;
-  const int64_t seg_off = is_k ? (int64_t)a.nq * a.d : 0;
-  uint16_t* base = a.qkv + token * a.I + seg_off + (int64_t)head * a.d;
+  if (hg >= ngroups) return;                // lanes past the last whole group (64 % cpd != 0)
 
-  float lo[8], hi[8];
-  unpack8(*reinterpret_cast<const uint4*>(base + j0), lo);
-  unpack8(*reinterpret_cast<const uint4*>(base + half + j0), hi);
-
-  const bool norm = is_k ? a.norm_k : a.norm_q;
-  if (norm) {
-    const int n = is_k ? a.nkv : a.nq;
-    const float ss = a.ssq[token * 2 + (is_k ? 1 : 0)];
-    const float r = 1.0f / sqrtf(ss / (float)(n * a.d) + a.eps);
-    const uint16_t* g = (is_k ? a.gk : a.gq) + (int64_t)head * a.d;
-    float glo[8], ghi[8];
-    unpack8(*reinterpret_cast<const uint4*>(g + j0), glo);
-    unpack8(*reinterpret_cast<const uint4*>(g + half + j0), ghi);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      lo[e] = lo[e] * (glo[e] * r);
-      hi[e] = hi[e] * (ghi[e] * r);
-    }
-  }
+  float clo[8], chi[8], slo[8], shi[8];
   if (a.rope) {
     const float* cr = a.cos_tab + token * a.d;
     const float* sr = a.sin_tab + token * a.d;
-    float clo[8], chi[8], slo[8], shi[8];
     load8f(cr + j0, clo);
     load8f(cr + half + j0, chi);
     load8f(sr + j0, slo);
     load8f(sr + half + j0, shi);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float ol = lo[e] * clo[e] - hi[e] * slo[e];
-      const float oh = hi[e] * chi[e] + lo[e] * shi[e];
-      lo[e] = ol;
-      hi[e] = oh;
-    }
   }
-  *reinterpret_cast<uint4*>(base + j0) = pack8(lo);
-  *reinterpret_cast<uint4*>(base + half + j0) = pack8(hi);
+  float rq = 1.0f, rk = 1.0f;
+  if (a.norm_q) rq = 1.0f / sqrtf(a.ssq[token * 2] / (float)(a.nq * a.d) + a.eps);
+  if (a.norm_k) rk = 1.0f / sqrtf(a.ssq[token * 2 + 1] / (float)(a.nkv * a.d) + a.eps);
+
+  uint16_t* row = a.qkv + token * a.I;
+#pragma unroll 4
+  for (int h = hg; h < a.heads; h += ngroups) {
+    const bool is_k = h >= a.heads_q;
+    // column of the head: Q heads come first; the K segment starts at nq * d
+    const int64_t col = is_k ? (int64_t)a.nq * a.d + (int64_t)(h - a.heads_q) * a.d
+                             : (int64_t)h * a.d;
+    uint16_t* base = row + col;
+    float lo[8], hi[8];
+    unpack8(*reinterpret_cast<const uint4*>(base + j0), lo);
+    unpack8(*reinterpret_cast<const uint4*>(base + half + j0), hi);
+    const bool norm = is_k ? a.norm_k : a.norm_q;
+    if (norm) {
+      const float r = is_k ? rk : rq;
+      const uint16_t* g = is_k ? a.gk + (int64_t)(h - a.heads_q) * a.d : a.gq + (int64_t)h * a.d;
+      float glo[8], ghi[8];
+      unpack8(*reinterpret_cast<const uint4*>(g + j0), glo);
+      unpack8(*reinterpret_cast<const uint4*>(g + half + j0), ghi);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        lo[e] = lo[e] * (glo[e] * r);
+        hi[e] = hi[e] * (ghi[e] * r);
+      }
+    }
+    if (a.rope) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ol = lo[e] * clo[e] - hi[e] * slo[e];
+        const float oh = hi[e] * chi[e] + lo[e] * shi[e];
+        lo[e] = ol;
+        hi[e] = oh;
+      }
+    }
+    __builtin_nontemporal_store(pack8(lo), reinterpret_cast<u32x4*>(base + j0));
+    __builtin_nontemporal_store(pack8(hi), reinterpret_cast<u32x4*>(base + half + j0));
+  }
 }
 
 }  // namespace
@@ -115,20 +133,15 @@ hipError_t launch_norm_rope(uint16_t* qkv, const float* ssq, const uint16_t* q_g
   a.sin_tab = sin_tab; a.T = T; a.I = (int64_t)(nq + 2 * nkv) * d;
   a.nq = nq; a.nkv = nkv; a.d = d; a.eps = eps;
   a.norm_q = flags & 1u; a.norm_k = (flags & 2u) && nkv > 0; a.rope = flags & 4u;
-  const int cpd = d / 16;
   const bool q_on = a.norm_q || a.rope;
   const bool k_on = nkv > 0 && (a.norm_k || a.rope);
-  a.units_q = q_on ? nq * cpd : 0;
-  a.units = a.units_q + (k_on ? nkv * cpd : 0);
-  if (a.units == 0 || T == 0) return hipSuccess;       // nothing to do
-  if (!q_on) {
-    // only K is touched: shift the K segment to unit 0 by treating it as "K" from the start
-    a.units_q = 0;
-  }
-  int bpt = (int)ceil_div(a.units, 512);
-  int block = (int)ceil_div(ceil_div(a.units, bpt), 64) * 64;
-  a.blocks_per_token = bpt;
-  hipLaunchKernelGGL(norm_rope_kernel, dim3((unsigned)(T * bpt)), dim3(block), 0, s, a);
+  a.heads_q = q_on ? nq : 0;
+  a.heads = a.heads_q + (k_on ? nkv : 0);
+  if (a.heads == 0 || T == 0) return hipSuccess;        // nothing to do
+  if (d / 16 > kThreadsPerToken) return hipErrorInvalidValue;
+  const int64_t blocks = ceil_div(T, kTokensPerBlock);
+  hipLaunchKernelGGL(norm_rope_kernel, dim3((unsigned)blocks),
+                     dim3(kThreadsPerToken * kTokensPerBlock), 0, s, a);
   return hipGetLastError();
 }
 

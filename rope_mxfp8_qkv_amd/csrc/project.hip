@@ -22,8 +22,9 @@
 //    issued from inline assembly with explicit vmcnt waits, because the compiler would
 //    otherwise wait for every outstanding DMA before each LDS read.
 //  * LDS image of a stage: 256 rows x 64 K-bytes, 16-byte chunk c of row r at chunk position
-//    c ^ ((r >> 1) & 3): a ds_read_b128 phase (8 lanes = 8 consecutive rows, one logical chunk)
-//    touches 8 distinct 16-byte bank groups.
+//    c ^ stage_swizzle(r): the 16 consecutive rows one ds_read_b128 serves at a logical chunk
+//    land on 16 distinct 16-byte bank groups of a 256-byte window (and any 8 aligned rows on
+//    8 distinct groups of a 128-byte window).
 //  * Epilogue: x = acc * a_scale[token] * c[channel] + bias[channel] in fp32, sums of x^2 per
 //    token over the Q and K columns (V excluded) written as one partial per 128 channels, bf16
 //    round-to-nearest-even, transposed through LDS so every global store is a coalesced
@@ -45,6 +46,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_a8 __attribute__((ext_vector_type(2), aligned(8)));
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;                         // token tiles per raster group
@@ -71,7 +73,7 @@ struct ProjectArgs {
 };
 
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * kStage + ((chunk ^ ((row >> 1) & 3)) << 4);
+  return row * kStage + ((chunk ^ stage_swizzle(row)) << 4);
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -203,12 +205,13 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   };
 
   // ---- software pipeline over K-steps of 64 bytes ----
-  // Step s: fragments of stage s are in registers [s & 1]; the step issues its 16 MFMAs
-  // while reading stage s + 1's fragments (and, on the last step of a superstep, the next
-  // superstep's exponents) and DMA-ing stage s + 4 into the buffer stage s occupied.  It ends
-  // by waiting for its own DMA of stage s + 2 (the most recent DMA groups, of stages s + 3 and
-  // s + 4, may stay in flight) and a barrier, after which stage s + 2 is complete in LDS for
-  // all waves and every wave has finished reading stage s + 1's buffer predecessor.
+  // Step s: fragments of stage s are in registers [s & 1].  The step first requests stage
+  // s + 4 into the buffer stage s occupied (every wave read stage s's fragments during step
+  // s - 1, before the barrier that ended it), then issues its 16 MFMAs while reading stage
+  // s + 1's fragments (and, on the last step of a superstep, the next superstep's exponents).
+  // It ends by waiting for its own DMA of stage s + 2 (the two most recent DMA groups, of
+  // stages s + 3 and s + 4, may stay in flight) and a barrier, after which stage s + 2 is
+  // complete in LDS for all waves.  Each stage thus has three steps to arrive.
   const int KS = a.KS;
   issue(std::integral_constant<int, 0>{}, 0);
   issue(std::integral_constant<int, 1>{}, 1);
@@ -228,6 +231,7 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     constexpr bool do_issue = decltype(issue_c)::value;
     constexpr int nwait = decltype(wait_c)::value;
     const int ssup = s >> 2;
+    if (do_issue) issue(q_c, s + 4);
     fload((s + 1) & (kBufs - 1), wf[p ^ 1], xf[p ^ 1]);
     if (q == 3) sload((ssup + 1) & 1, sc[1]);
 #pragma unroll
@@ -241,7 +245,6 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
-    if (do_issue) issue(q_c, s + 4);
     if (q == 3) {
 #pragma unroll
       for (int cf = 0; cf < 4; ++cf) sc[0][cf] = sc[1][cf];
@@ -275,7 +278,9 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   // ---- epilogue ----
   // x = acc * a_scale * c + bias (fp32) -> sums of squares from the fp32 values, bf16 into a
   // per-wave 128 x 128 LDS tile (token rows of 256 bytes, 16-byte chunk j of row r at chunk
-  // position j ^ (r & 15)), then read back row-contiguous and stored as 16-byte vectors.
+  // position j ^ (r & 15), its two 8-byte halves swapped when bit 4 of r is set, so the 32
+  // rows of one 8-byte store phase hit distinct banks), then read back row-contiguous and
+  // stored as 16-byte vectors.
   __builtin_amdgcn_sched_barrier(0);
   uint8_t* const otile = (wm == 0 ? &lds_w[0][0] : &lds_x[0][0]) + wn * 32768;
   float sq_q[4] = {0.f, 0.f, 0.f, 0.f}, sq_k[4] = {0.f, 0.f, 0.f, 0.f};
@@ -302,7 +307,8 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
         const int row = tf * 32 + fr;
         const int chunk = cf * 4 + rq;
         u32x2_a8 o = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-        *reinterpret_cast<u32x2_a8*>(otile + row * 256 + ((chunk ^ (row & 15)) << 4) + g * 8) = o;
+        *reinterpret_cast<u32x2_a8*>(otile + row * 256 + ((chunk ^ (row & 15)) << 4) +
+                                     ((g ^ (row >> 4)) & 1) * 8) = o;
       }
     }
   }
@@ -326,15 +332,20 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
 #pragma unroll 4
   for (int it = 0; it < 32; ++it) {
     const int row = it * 4 + (lane >> 4);
-    const uint4 v = *reinterpret_cast<const uint4*>(otile + row * 256 + ((jc ^ (row & 15)) << 4));
+    uint4 v = *reinterpret_cast<const uint4*>(otile + row * 256 + ((jc ^ (row & 15)) << 4));
+    if ((row >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);   // halves stored swapped
     const int64_t tok = m0 + wm * 128 + row;
-    if (ch_ok && tok < a.T) *reinterpret_cast<uint4*>(a.out + tok * a.I + ch) = v;
+    // streaming store (non-temporal): the output is not re-read by this kernel, and keeping
+    // it out of L2 leaves L2 to the operand stage images that neighbouring tiles share
+    if (ch_ok && tok < a.T)
+      __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
+                                  reinterpret_cast<u32x4*>(a.out + tok * a.I + ch));
   }
 }
 
 // Activation codes [T, stride] (rows only 4-byte aligned in the packed [T, H + 4] layout) ->
 // the stage images the projection DMA-copies: per (token tile tm, K-stage t) 256 rows x 64
-// bytes with 16-byte chunk c of row r at chunk position c ^ ((r >> 1) & 3); zero past T or H.
+// bytes with 16-byte chunk c of row r at chunk position c ^ stage_swizzle(r); zero past T or H.
 // One thread per 16-byte position.
 __global__ void __launch_bounds__(256) act_repack_kernel(const uint8_t* __restrict__ a,
                                                          int64_t stride, int64_t T, int64_t H,
@@ -343,7 +354,7 @@ __global__ void __launch_bounds__(256) act_repack_kernel(const uint8_t* __restri
   const int64_t t = blockIdx.y;
   const int64_t tm = blockIdx.z;
   const int r = p >> 2;
-  const int c = (p & 3) ^ ((r >> 1) & 3);
+  const int c = (p & 3) ^ stage_swizzle(r);
   const int64_t m = tm * kTileM + r;
   const int64_t k = t * kStage + 16 * c;
   uint4 o = make_uint4(0, 0, 0, 0);

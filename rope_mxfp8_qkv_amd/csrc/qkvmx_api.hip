@@ -155,6 +155,7 @@ qkvmx_status qk_norm_rope_apply(uint16_t* qkv, const float* ssq, const uint16_t*
   if (T <= 0 || num_heads < 1 || num_kv_heads < 0 || head_dim <= 0 || head_dim % 16)
     return fail(QKVMX_ERR_SHAPE, "qk_norm_rope_apply: need T > 0, num_heads >= 1, num_kv_heads >= 0, head_dim %% 16 == 0");
   if (layout != QKVMX_LAYOUT_BSD) return fail(QKVMX_ERR_UNSUPPORTED, "qk_norm_rope_apply: only the BSD layout is built");
+  if (head_dim > 1024) return fail(QKVMX_ERR_UNSUPPORTED, "qk_norm_rope_apply: head_dim > 1024");
   if ((flags & QKVMX_FUSED_ROPE) && (!cos_tab || !sin_tab))
     return fail(QKVMX_ERR_ARG, "qk_norm_rope_apply: QKVMX_FUSED_ROPE needs cos_tab and sin_tab");
   if (num_kv_heads == 0 && ((flags & QKVMX_NORM_K) || k_gamma))

@@ -49,7 +49,7 @@ __global__ void __launch_bounds__(256) mx_weight_quantize_kernel(const float* __
 }
 
 // Codes: one thread per 16-byte chunk position p (0..1023) of the stage image (tile tn, stage
-// t): position p holds logical chunk c = (p % 4) ^ ((r >> 1) & 3) of row r = p / 4, i.e. bytes
+// t): position p holds logical chunk c = (p % 4) ^ stage_swizzle(r) of row r = p / 4, i.e. bytes
 // [64 t + 16 c, +16) of channel 256 tn + r, gathered from four dwords of the [H/4, I, 4] codes
 // (h/4 rows 16 t + 4 c .. +3).  Zero past I or H.
 __global__ void __launch_bounds__(256) prepack_codes_kernel(const uint8_t* __restrict__ codes,
@@ -59,7 +59,7 @@ __global__ void __launch_bounds__(256) prepack_codes_kernel(const uint8_t* __res
   const int64_t t = blockIdx.y;
   const int64_t tn = blockIdx.z;
   const int r = p >> 2;
-  const int c = (p & 3) ^ ((r >> 1) & 3);
+  const int c = (p & 3) ^ stage_swizzle(r);
   const int64_t n = tn * kTileN + r;
   const int64_t k = t * kStage + 16 * c;
   uint4 o = make_uint4(0, 0, 0, 0);
