@@ -224,32 +224,54 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   wait_vm<2 * kDmaPerStage>();
   __syncthreads();
 
+  // One K-step as 16 issue slots, each one MFMA followed by one fragment read for the next
+  // step and (in the first slots) one DMA request, separated by hard scheduling barriers: the
+  // DMAs of the four wavefronts then trickle out one per MFMA instead of arriving at the
+  // address unit as one burst after the barrier, and every MFMA has independent work behind it.
   auto step = [&](auto q_c, int s, auto issue_c, auto wait_c) {
     constexpr int q = decltype(q_c)::value;        // step within the 256-K superstep
     constexpr int p = q & 1;
-    constexpr int sp = (q == 3) ? 1 : 0;           // exponent set of the next step
     constexpr bool do_issue = decltype(issue_c)::value;
     constexpr int nwait = decltype(wait_c)::value;
-    const int ssup = s >> 2;
-    if (do_issue) issue(q_c, s + 4);
-    fload((s + 1) & (kBufs - 1), wf[p ^ 1], xf[p ^ 1]);
-    if (q == 3) sload((ssup + 1) & 1, sc[1]);
+    const int nb = (s + 1) & (kBufs - 1);          // buffer of stage s + 1
+    const int t = s + 4;                           // stage requested by this step
+    const uint32_t k_img = (uint32_t)t * kStageImage;
 #pragma unroll
-    for (int cf = 0; cf < 4; ++cf)
-#pragma unroll
-      for (int tf = 0; tf < 4; ++tf)
-        acc[cf][tf] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            wf[p][cf], xf[p][tf], acc[cf][tf], 0, 0, q, (int)sc[0][cf], 0, 0x7F7F7F7F);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    for (int k = 0; k < 16; ++k) {
+      const int cf = k >> 2, tf = k & 3;
+      acc[cf][tf] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          wf[p][cf], xf[p][tf], acc[cf][tf], 0, 0, q, (int)sc[0][cf], 0, 0x7F7F7F7F);
+      // fragment k / 2 of stage s + 1: even k -> weight fragment, odd k -> activation fragment
+      const int f = k >> 2, half = (k >> 1) & 1;
+      if ((k & 1) == 0) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&lds_w[nb][(half ? rw1 : rw0) + 2048 * f]);
+        if (half == 0) { wf[p ^ 1][f][0] = (int)v.x; wf[p ^ 1][f][1] = (int)v.y; wf[p ^ 1][f][2] = (int)v.z; wf[p ^ 1][f][3] = (int)v.w; }
+        else { wf[p ^ 1][f][4] = (int)v.x; wf[p ^ 1][f][5] = (int)v.y; wf[p ^ 1][f][6] = (int)v.z; wf[p ^ 1][f][7] = (int)v.w; }
+      } else {
+        const uint4 v = *reinterpret_cast<const uint4*>(&lds_x[nb][(half ? rx1 : rx0) + 2048 * f]);
+        if (half == 0) { xf[p ^ 1][f][0] = (int)v.x; xf[p ^ 1][f][1] = (int)v.y; xf[p ^ 1][f][2] = (int)v.z; xf[p ^ 1][f][3] = (int)v.w; }
+        else { xf[p ^ 1][f][4] = (int)v.x; xf[p ^ 1][f][5] = (int)v.y; xf[p ^ 1][f][6] = (int)v.z; xf[p ^ 1][f][7] = (int)v.w; }
+      }
+      if (do_issue) {
+        if (k < 8) {
+          const int i = k >> 1;
+          if ((k & 1) == 0)
+            dma16(wdst + q * kStageImage + i * 1024, wsrc + k_img + i * 1024);
+          else
+            dma16(xdst + q * kStageImage + i * 1024, xsrc + k_img + i * 1024);
+        } else if (q == 0 && (k == 8 || k == 9)) {
+          const int64_t sup = t >> 2;
+          const uint32_t slot = sdst + (uint32_t)(sup & 1) * 2048;
+          dma4(slot + (k - 8) * 256, ssrc + sup * s_step + (k - 8) * 256);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (q == 3) {
+      sload(((s >> 2) + 1) & 1, sc[1]);
 #pragma unroll
       for (int cf = 0; cf < 4; ++cf) sc[0][cf] = sc[1][cf];
     }
-    (void)sp;
     if (nwait >= 0) wait_vm<(nwait < 0 ? 0 : nwait)>();
     __syncthreads();
   };
