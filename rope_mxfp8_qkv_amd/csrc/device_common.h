@@ -10,16 +10,13 @@ namespace qkvmx {
 // bf16 bits -> fp32 (exact widening).
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// fp32 -> bf16 bits, round to nearest, ties to even.  Inputs are finite on every path.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-// Two fp32 -> packed bf16x2 (low half = a).
+// Two fp32 -> packed bf16x2 (low half = a), round to nearest, ties to even: one
+// V_CVT_PK_BF16_F32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 // fp32 -> FP8 E4M3 ("fn": max 448, no infinities), round to nearest even, saturating at +-448.

@@ -26,10 +26,10 @@
 //    land on 16 distinct 16-byte bank groups of a 256-byte window (and any 8 aligned rows on
 //    8 distinct groups of a 128-byte window).
 //  * Epilogue: x = acc * a_scale[token] * c[channel] + bias[channel] in fp32, sums of x^2 per
-//    token over the Q and K columns (V excluded) written as one partial per 128 channels, bf16
-//    round-to-nearest-even, transposed through LDS so every global store is a coalesced
-//    16-byte vector along a token row.  A small second kernel adds the partials in a fixed order
-//    (deterministic, no atomics).
+//    token over the Q and K columns (V excluded) written as one partial per 128 channels
+//    (groups holding only V write none), bf16 round-to-nearest-even (V_CVT_PK_BF16_F32),
+//    transposed through LDS so every global store is a coalesced 16-byte vector along a token
+//    row.  A small second kernel adds the partials in a fixed order (deterministic, no atomics).
 //  * Tile order: block ids are dealt round-robin to the 8 XCDs; they are remapped so that each
 //    XCD owns a contiguous range of tiles, walked in groups of 8 token tiles x all channel tiles,
 //    so the tiles resident on one XCD share activation rows and weight columns in its L2.
@@ -97,6 +97,7 @@ __device__ __forceinline__ void wait_vm() {
 // Instruction-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
+template <bool kChanScale>
 __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_w[kBufs][kStageImage];
   __shared__ __attribute__((aligned(16))) uint8_t lds_x[kBufs][kStageImage];
@@ -305,27 +306,46 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   // stored as 16-byte vectors.
   __builtin_amdgcn_sched_barrier(0);
   uint8_t* const otile = (wm == 0 ? &lds_w[0][0] : &lds_x[0][0]) + wn * 32768;
+  // the epilogue's operands go to registers first, under one LDS wait: the row scales of this
+  // lane's 4 tokens and the bias (and channel scale) of its 16 channel quads
+  float sa[4];
+#pragma unroll
+  for (int tf = 0; tf < 4; ++tf) sa[tf] = lds_sa[wm * 128 + tf * 32 + fr];
+  float4 bq[4][4], cq[4][4];
+#pragma unroll
+  for (int cf = 0; cf < 4; ++cf)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int cl = cf * 32 + rq * 8 + g * 4;
+      bq[cf][rq] = *reinterpret_cast<const float4*>(&lds_bias[wn * 128 + cl]);
+      if (kChanScale) cq[cf][rq] = *reinterpret_cast<const float4*>(&lds_cs[wn * 128 + cl]);
+    }
   float sq_q[4] = {0.f, 0.f, 0.f, 0.f}, sq_k[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int cf = 0; cf < 4; ++cf) {
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       const int cl = cf * 32 + rq * 8 + g * 4;            // 4 consecutive channels (local)
-      const float4 c4 = *reinterpret_cast<const float4*>(&lds_cs[wn * 128 + cl]);
-      const float4 b4 = *reinterpret_cast<const float4*>(&lds_bias[wn * 128 + cl]);
-      const float cs[4] = {c4.x, c4.y, c4.z, c4.w}, bs[4] = {b4.x, b4.y, b4.z, b4.w};
+      const float bs[4] = {bq[cf][rq].x, bq[cf][rq].y, bq[cf][rq].z, bq[cf][rq].w};
+      float cs[4] = {1.f, 1.f, 1.f, 1.f};
+      if (kChanScale) {
+        cs[0] = cq[cf][rq].x; cs[1] = cq[cf][rq].y; cs[2] = cq[cf][rq].z; cs[3] = cq[cf][rq].w;
+      }
       const int64_t ng = n0 + wn * 128 + cl;
-      const bool in_q = ng < a.Iq;
-      const bool in_k = !in_q && ng < a.Iq + a.Ik;
+      // 0/1 masks of the Q and K segments (multiplies rather than branches keep the epilogue
+      // straight-line code)
+      const float mq = ng < a.Iq ? 1.f : 0.f;
+      const float mk = ng >= a.Iq && ng < a.Iq + a.Ik ? 1.f : 0.f;
 #pragma unroll
       for (int tf = 0; tf < 4; ++tf) {
-        const float sa = lds_sa[wm * 128 + tf * 32 + fr];
         float x[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = acc[cf][tf][rq * 4 + e] * sa * cs[e] + bs[e];
+        for (int e = 0; e < 4; ++e)
+          x[e] = kChanScale ? acc[cf][tf][rq * 4 + e] * sa[tf] * cs[e] + bs[e]
+                            : fmaf(acc[cf][tf][rq * 4 + e], sa[tf], bs[e]);
         const float s2 = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
-        if (in_q) sq_q[tf] += s2;
-        if (in_k) sq_k[tf] += s2;
+        sq_q[tf] = fmaf(mq, s2, sq_q[tf]);
+        sq_k[tf] = fmaf(mk, s2, sq_k[tf]);
         const int row = tf * 32 + fr;
         const int chunk = cf * 4 + rq;
         u32x2_a8 o = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
@@ -334,7 +354,7 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
       }
     }
   }
-  if (a.ws) {
+  if (a.ws && n0 + wn * 128 < a.Iq + a.Ik) {        // this wave's channels overlap Q or K
     const int64_t p = (int64_t)tn * 2 + wn;
 #pragma unroll
     for (int tf = 0; tf < 4; ++tf) {
@@ -347,22 +367,40 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
       }
     }
   }
-  // row-contiguous read-back: 16 lanes per 256-byte token row, 4 rows per instruction
+  // row-contiguous read-back: 16 lanes per 256-byte token row, 4 rows per instruction (rows
+  // 4 it .. 4 it + 3); eight LDS reads are in flight before their eight stores.  Streaming
+  // (non-temporal) stores: the output is not re-read by this kernel, and keeping it out of L2
+  // leaves L2 to the operand stage images that neighbouring tiles share.
   const int jc = lane & 15;
   const int64_t ch = n0 + wn * 128 + jc * 8;
-  const bool ch_ok = ch < a.I;
-#pragma unroll 4
-  for (int it = 0; it < 32; ++it) {
-    const int row = it * 4 + (lane >> 4);
-    uint4 v = *reinterpret_cast<const uint4*>(otile + row * 256 + ((jc ^ (row & 15)) << 4));
-    if ((row >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);   // halves stored swapped
-    const int64_t tok = m0 + wm * 128 + row;
-    // streaming store (non-temporal): the output is not re-read by this kernel, and keeping
-    // it out of L2 leaves L2 to the operand stage images that neighbouring tiles share
-    if (ch_ok && tok < a.T)
-      __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
-                                  reinterpret_cast<u32x4*>(a.out + tok * a.I + ch));
-  }
+  const int64_t tok0 = m0 + wm * 128 + (lane >> 4);
+  uint16_t* const obase = a.out + tok0 * a.I + ch;
+  auto store_rows = [&](auto check_c) {
+    constexpr bool kCheck = decltype(check_c)::value;
+    const bool ch_ok = ch < a.I;
+#pragma unroll
+    for (int b8 = 0; b8 < 4; ++b8) {
+      uint4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = (b8 * 8 + j) * 4 + (lane >> 4);
+        v[j] = *reinterpret_cast<const uint4*>(otile + row * 256 + ((jc ^ (row & 15)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int it = b8 * 8 + j;
+        // bit 4 of the row is bit 2 of it: those rows hold their 8-byte halves swapped
+        const u32x4 o = ((it >> 2) & 1) ? u32x4{v[j].z, v[j].w, v[j].x, v[j].y}
+                                        : u32x4{v[j].x, v[j].y, v[j].z, v[j].w};
+        if (!kCheck || (ch_ok && tok0 + it * 4 < a.T))
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(obase + (int64_t)it * 4 * a.I));
+      }
+    }
+  };
+  if (m0 + kTileM <= a.T && n0 + kTileN <= a.I)      // whole tile inside the output
+    store_rows(std::false_type{});
+  else
+    store_rows(std::true_type{});
 }
 
 // Activation codes [T, stride] (rows only 4-byte aligned in the packed [T, H + 4] layout) ->
@@ -387,7 +425,7 @@ __global__ void __launch_bounds__(256) act_repack_kernel(const uint8_t* __restri
   reinterpret_cast<uint4*>(img)[(tm * KS + t) * (kStageImage / 16) + p] = o;
 }
 
-// ssq[t] = sum over partials p of ws[p][t] (fixed order).
+// ssq[t] = sum over partials p < P of ws[p][t] (fixed order); P = 0 gives zeros.
 __global__ void __launch_bounds__(256) ssq_reduce_kernel(const float* __restrict__ ws, int64_t P,
                                                          int64_t T, float* __restrict__ ssq) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -425,10 +463,14 @@ hipError_t launch_project(const uint8_t* a_codes, int64_t a_stride, const uint8_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned nblocks = (unsigned)(a.tiles_m * a.tiles_n);
-  hipLaunchKernelGGL(project_kernel, dim3(nblocks), dim3(kThreads), 0, s, a);
+  if (chan_scale)
+    hipLaunchKernelGGL(project_kernel<true>, dim3(nblocks), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(project_kernel<false>, dim3(nblocks), dim3(kThreads), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess || !ssq) return e;
-  const int64_t P = ssq_partials(I);
+  // only the partials of 128-channel groups that overlap Q or K are written and summed
+  const int64_t P = ceil_div(Iq + Ik, (int64_t)kPartialN);
   hipLaunchKernelGGL(ssq_reduce_kernel, dim3((unsigned)ceil_div(T, 256)), dim3(256), 0, s,
                      partials, P, T, ssq);
   return hipGetLastError();

@@ -136,11 +136,10 @@ __global__ void __launch_bounds__(1024) rmsnorm_quantize_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           // r = bf16_RNE(fp32 + fp32): one fp32 rounding, then one bf16 rounding
-          const uint32_t lo = f32_to_bf16(bf16_to_f32(hw[e] & 0xFFFFu) + bf16_to_f32(rw[e] & 0xFFFFu));
-          const uint32_t hi = f32_to_bf16(bf16_to_f32(hw[e] >> 16) + bf16_to_f32(rw[e] >> 16));
-          ow[e] = lo | (hi << 16);
-          y[k][2 * e] = bf16_to_f32(lo);
-          y[k][2 * e + 1] = bf16_to_f32(hi);
+          ow[e] = pack_bf16x2(bf16_to_f32(hw[e] & 0xFFFFu) + bf16_to_f32(rw[e] & 0xFFFFu),
+                              bf16_to_f32(hw[e] >> 16) + bf16_to_f32(rw[e] >> 16));
+          y[k][2 * e] = bf16_to_f32(ow[e] & 0xFFFFu);
+          y[k][2 * e + 1] = bf16_to_f32(ow[e] >> 16);
         }
         reinterpret_cast<uint4*>(res_out + row * H)[c] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
       } else {
