@@ -33,6 +33,7 @@
 //  * Tile order: block ids are dealt round-robin to the 8 XCDs; they are remapped so that each
 //    XCD owns a contiguous range of tiles, walked in groups of 8 token tiles x all channel tiles,
 //    so the tiles resident on one XCD share activation rows and weight columns in its L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -52,6 +53,8 @@ constexpr int kThreads = 256;
 constexpr int kGroupM = 8;                         // token tiles per raster group
 constexpr int kXcds = 8;
 constexpr int kBufs = 4;                           // LDS stage buffers
+constexpr int kBufferRsrcWord3 = 0x00020000;        // buffer descriptor word 3 (gfx9 family)
+constexpr int kNonTemporal = 2;                    // buffer store cache policy: streaming
 constexpr int kDmaPerStage = 8;                    // per wave: 4 (weight) + 4 (activation)
                                                    // (+ 2 exponent DMAs every 4th stage)
 
@@ -80,15 +83,53 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)(p);
 }
 
-// Global -> LDS DMA of 16 bytes per lane (lane L lands at lds + 16 L) / 4 bytes per lane.
-__device__ __forceinline__ void dma16(uint32_t lds, const void* g) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds), "v"(g) : "memory", "m0");
+// Global -> LDS DMA in the scalar-base form: lane L reads sbase + voff_L (+ the immediate
+// offset) and writes LDS at M0 (+ the immediate offset) + 16 L (dwordx4) or + 4 L (dword).
+// The wave-uniform part of every source address stays in SGPRs; the only vector operand is
+// the lane's byte offset.
+//
+// 1 KiB block i (0..3) of a stage image: the immediate offset 1024 i is added to both the
+// global and the LDS address, so M0 only carries the stage buffer (base + Q * kStageImage);
+// the switch folds away once i is a constant.
+template <int Q>
+__device__ __forceinline__ void dma16_blk(uint32_t base, const uint8_t* sbase, uint32_t voff,
+                                          int i) {
+#define QKVMX_DMA_BLK(OFF)                                                                  \
+  asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:" #OFF \
+               :: "s"(base), "v"(voff), "s"(sbase), "n"(Q * kStageImage) : "memory", "m0", "scc")
+  switch (i) {
+    case 0: QKVMX_DMA_BLK(0); break;
+    case 1: QKVMX_DMA_BLK(1024); break;
+    case 2: QKVMX_DMA_BLK(2048); break;
+    default: QKVMX_DMA_BLK(3072); break;
+  }
+#undef QKVMX_DMA_BLK
 }
-__device__ __forceinline__ void dma4(uint32_t lds, const void* g) {
+// Dword DMA from a per-lane 64-bit address (lane L: 4 bytes from g_L to LDS lds + 4 L).
+__device__ __forceinline__ void dma4g(uint32_t lds, const void* g) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
                :: "s"(lds), "v"(g) : "memory", "m0");
 }
+__device__ __forceinline__ void dma4(uint32_t lds, const uint8_t* sbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+// The lane index, computed afresh (V_MBCNT) where it is needed: as volatile asm it is neither
+// merged with an earlier copy nor hoisted, so lane-derived values need no register (or spill
+// slot) across the K-steps.
+__device__ __forceinline__ int fresh_lane() {
+  int r;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(r));
+  return r;
+}
+
+// v + (v of lane ^ 32): the two lane halves' partial sums combined (ds_bpermute addressed from
+// a fresh lane index).
+__device__ __forceinline__ float add_xor32(float v) {
+  const int src = (fresh_lane() ^ 32) << 2;
+  return v + __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v)));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
@@ -97,16 +138,31 @@ __device__ __forceinline__ void wait_vm() {
 // Instruction-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
+// Token tile and channel tile of tile index `tile` in the grouped raster order: groups of
+// kGroupM token tiles, walked channel tile by channel tile.
+struct Tile {
+  int tm, tn;
+};
+__device__ __forceinline__ Tile decode_tile(int tile, int tiles_m, int tiles_n) {
+  const int group = tile / (kGroupM * tiles_n);
+  const int first_m = group * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int in_group = tile % (kGroupM * tiles_n);
+  return Tile{first_m + in_group % gm, in_group / gm};
+}
+
 template <bool kChanScale>
 __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_w[kBufs][kStageImage];
   __shared__ __attribute__((aligned(16))) uint8_t lds_x[kBufs][kStageImage];
   __shared__ __attribute__((aligned(16))) uint8_t lds_sc[2][kTileN * 8];
-  // epilogue operands of this block: channel scale and bias (fp32) per channel, row scale per
-  // token; staged once so the epilogue reads them from LDS
-  __shared__ __attribute__((aligned(16))) float lds_cs[kTileN];
-  __shared__ __attribute__((aligned(16))) float lds_bias[kTileN];
-  __shared__ __attribute__((aligned(16))) float lds_sa[kTileM];
+  // epilogue operands, double-buffered (the next tile's arrive while the current tile's are
+  // in use): channel scale and row scale (fp32) and the bias, DMA-copied as raw bf16 pairs and
+  // widened to fp32 at the start of the tile
+  __shared__ __attribute__((aligned(16))) float lds_cs[2][kTileN];
+  __shared__ __attribute__((aligned(16))) float lds_sa[2][kTileM];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_braw[2][kTileN / 2];
+  __shared__ __attribute__((aligned(16))) float lds_bias[2][kTileN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -114,76 +170,105 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   const int wn = wave & 1;        // channel half of the block tile
   const int wm = wave >> 1;       // token half
 
-  // ---- tile id: XCD-contiguous ranges, grouped raster ----
+  // ---- tiles of this block: XCD-contiguous ranges, visited with a stride of the XCD's blocks
   const int ntiles = a.tiles_m * a.tiles_n;
   const int b = blockIdx.x;
-  const int xcd = b % kXcds, k_in = b / kXcds;
+  const int xcd = b % kXcds;
   const int per = ntiles / kXcds, rem = ntiles % kXcds;
-  const int tile = xcd < rem ? xcd * (per + 1) + k_in : rem * (per + 1) + (xcd - rem) * per + k_in;
-  const int group = tile / (kGroupM * a.tiles_n);
-  const int first_m = group * kGroupM;
-  const int gm = min(a.tiles_m - first_m, kGroupM);
-  const int in_group = tile % (kGroupM * a.tiles_n);
-  const int tm = first_m + in_group % gm;
-  const int tn = in_group / gm;
-  const int64_t m0 = (int64_t)tm * kTileM;
-  const int64_t n0 = (int64_t)tn * kTileN;
+  const int xcd_first = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+  const int xcd_count = per + (xcd < rem ? 1 : 0);
+  const int xcd_blocks = ((int)gridDim.x - xcd + kXcds - 1) / kXcds;
+  int k_in = b / kXcds;
+  if (k_in >= xcd_count) return;          // the whole block, before any barrier
+  Tile t = decode_tile(xcd_first + k_in, a.tiles_m, a.tiles_n);
 
-  {
-    const int64_t n = min(n0 + tid, a.I - 1);
-    lds_cs[tid] = a.chan_scale ? a.chan_scale[n] : 1.0f;
-    lds_bias[tid] = a.bias ? bf16_to_f32(a.bias[n]) : 0.0f;
-    const int64_t t = min(m0 + tid, a.T - 1);
-    lds_sa[tid] = *reinterpret_cast<const float*>(a.a_scales + t * a.s_stride);
-  }
-
-  // ---- DMA sources ----
-  // weight: wave w copies 1 KiB blocks 4 w .. 4 w + 3 of each 16 KiB stage image
-  const uint8_t* wsrc = a.w_img + ((int64_t)tn * a.KS) * kStageImage + wave * 4096 + lane * 16;
-  const uint32_t wdst = lds_addr(&lds_w[0][0]) + wave * 4096;
-  // exponents: each wave copies 512 bytes (two dword DMAs) of the 2 KiB per superstep
-  const uint8_t* ssrc = a.w_scales + ((int64_t)tn * kTileN * 2) * 4 + wave * 512 + lane * 4;
-  const int64_t s_step = (int64_t)a.tiles_n * kTileN * 2 * 4;       // bytes per superstep
-  const uint32_t sdst = lds_addr(&lds_sc[0][0]) + wave * 512;
+  // ---- DMA sources of the current tile (wave-uniform bases, in SGPRs) ----
+  // weight: wave w copies 1 KiB blocks 4 w .. 4 w + 3 of each 16 KiB stage image;
+  // exponents: each wave copies 512 bytes (two dword DMAs) of the 2 KiB per superstep;
   // activation: same scheme as the weight, from the per-call stage images
-  const uint8_t* xsrc = a.x_img + ((int64_t)tm * a.KS) * kStageImage + wave * 4096 + lane * 16;
+  const uint32_t wdst = lds_addr(&lds_w[0][0]) + wave * 4096;
   const uint32_t xdst = lds_addr(&lds_x[0][0]) + wave * 4096;
+  const uint32_t sdst = lds_addr(&lds_sc[0][0]) + wave * 512;
+  const int64_t s_step = (int64_t)a.tiles_n * kTileN * 2 * 4;       // bytes per superstep
+  const uint8_t* wbase;
+  const uint8_t* xbase;
+  const uint8_t* sbase;
+  auto set_sources = [&](Tile u) {
+    wbase = a.w_img + ((int64_t)u.tn * a.KS) * kStageImage + wave * 4096;
+    sbase = a.w_scales + ((int64_t)u.tn * kTileN * 2) * 4 + wave * 512;
+    xbase = a.x_img + ((int64_t)u.tm * a.KS) * kStageImage + wave * 4096;
+  };
+  set_sources(t);
 
   // DMA of stage t (t % 4 == Q) into buffer Q; a stage opening a superstep also brings that
   // superstep's exponents into ring slot (t / 4) % 2.
   auto issue = [&](auto q_c, int t) {
     constexpr int Q = decltype(q_c)::value;
+    const uint32_t lv = fresh_lane();
+    const uint32_t voff16 = lv * 16, voff4 = lv * 4;
     if (Q == 0) {
       const int64_t sup = t >> 2;
       const uint32_t slot = sdst + (uint32_t)(sup & 1) * 2048;
-      dma4(slot, ssrc + sup * s_step);
-      dma4(slot + 256, ssrc + sup * s_step + 256);
+      dma4(slot, sbase + sup * s_step, voff4);
+      dma4(slot + 256, sbase + sup * s_step + 256, voff4);
     }
+    const uint8_t* const wsrc_t = wbase + (int64_t)t * kStageImage;
+    const uint8_t* const xsrc_t = xbase + (int64_t)t * kStageImage;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      dma16(wdst + Q * kStageImage + i * 1024, wsrc + (int64_t)t * kStageImage + i * 1024);
-      dma16(xdst + Q * kStageImage + i * 1024, xsrc + (int64_t)t * kStageImage + i * 1024);
+      dma16_blk<Q>(wdst, wsrc_t, voff16, i);
+      dma16_blk<Q>(xdst, xsrc_t, voff16, i);
     }
   };
 
+  // DMA of tile u's epilogue operands into operand buffer e (one dword per lane, indices
+  // clamped to the last row / channel): wave w brings the row scales of tokens 64 w ..
+  // 64 w + 63 and the channel scales of channels 64 w .. 64 w + 63; waves 0 and 1 bring the
+  // 128 bf16 pairs of the tile's bias.
+  auto issue_ops = [&](Tile u, int e) {
+    const int lv = fresh_lane();
+    const int64_t m = min((int64_t)u.tm * kTileM + wave * 64 + lv, a.T - 1);
+    dma4g(lds_addr(&lds_sa[e][wave * 64]), a.a_scales + m * a.s_stride);
+    if (kChanScale) {
+      const int64_t n = min((int64_t)u.tn * kTileN + wave * 64 + lv, a.I - 1);
+      dma4g(lds_addr(&lds_cs[e][wave * 64]), a.chan_scale + n);
+    }
+    if (a.bias && wave < 2) {
+      const int64_t n2 = min((int64_t)u.tn * kTileN + 2 * (wave * 64 + lv), a.I - 2);
+      dma4g(lds_addr(&lds_braw[e][wave * 64]), a.bias + n2);
+    }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using Yes = std::true_type;
+  using No = std::false_type;
+  using W40 = std::integral_constant<int, 2 * kDmaPerStage>;
+  using W20 = std::integral_constant<int, kDmaPerStage>;
+  using W0 = std::integral_constant<int, 0>;
+  using WN = std::integral_constant<int, -1>;
+
+  // lane-derived LDS offsets of the K-steps, recomputed at the start of every tile (from a
+  // fresh lane index) so that none of them is live across the epilogue
+  int rw0, rw1, rx0, rx1, rsc;
+  uint32_t kvoff16;
+  auto set_lane_offsets = [&]() {
+    const int lv = fresh_lane();
+    const int g = lv >> 5;
+    const int fr = lv & 31;             // fragment row of this lane
+    const int w_row0 = wn * 128 + fr;   // + 32 cf
+    const int x_row0 = wm * 128 + fr;   // + 32 tf
+    // the two 16-byte halves a lane feeds to the MFMA: chunks g and 2 + g of its row; rows
+    // 32 f apart share the swizzle, so fragment f sits 32 * 64 * f bytes further on
+    rw0 = lds_off(w_row0, g); rw1 = lds_off(w_row0, 2 + g);
+    rx0 = lds_off(x_row0, g); rx1 = lds_off(x_row0, 2 + g);
+    rsc = (w_row0 * 2 + g) * 4;         // + 32 * 8 cf: this lane's exponent dword
+    kvoff16 = lv * 16;
+  };
+
   v16f acc[4][4];
-#pragma unroll
-  for (int cf = 0; cf < 4; ++cf)
-#pragma unroll
-    for (int tf = 0; tf < 4; ++tf)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[cf][tf][r] = 0.0f;
-
-  const int g = lane >> 5;
-  const int fr = lane & 31;           // fragment row of this lane
-  const int w_row0 = wn * 128 + fr;   // + 32 cf
-  const int x_row0 = wm * 128 + fr;   // + 32 tf
-  // the two 16-byte halves a lane feeds to the MFMA: chunks g and 2 + g of its row; rows
-  // 32 f apart share the swizzle, so fragment f sits 32 * 64 * f bytes further on
-  const int rw0 = lds_off(w_row0, g), rw1 = lds_off(w_row0, 2 + g);
-  const int rx0 = lds_off(x_row0, g), rx1 = lds_off(x_row0, 2 + g);
-  const int rsc = (w_row0 * 2 + g) * 4;   // + 32 * 8 cf: this lane's exponent dword
-
   v8i wf[2][4], xf[2][4];
   uint32_t sc[2][4];
   auto fload = [&](int buf, v8i (&wd)[4], v8i (&xd)[4]) {
@@ -206,37 +291,28 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   };
 
   // ---- software pipeline over K-steps of 64 bytes ----
-  // Step s: fragments of stage s are in registers [s & 1].  The step first requests stage
-  // s + 4 into the buffer stage s occupied (every wave read stage s's fragments during step
-  // s - 1, before the barrier that ended it), then issues its 16 MFMAs while reading stage
-  // s + 1's fragments (and, on the last step of a superstep, the next superstep's exponents).
-  // It ends by waiting for its own DMA of stage s + 2 (the two most recent DMA groups, of
-  // stages s + 3 and s + 4, may stay in flight) and a barrier, after which stage s + 2 is
-  // complete in LDS for all waves.  Each stage thus has three steps to arrive.
-  const int KS = a.KS;
-  issue(std::integral_constant<int, 0>{}, 0);
-  issue(std::integral_constant<int, 1>{}, 1);
-  issue(std::integral_constant<int, 2>{}, 2);
-  issue(std::integral_constant<int, 3>{}, 3);
-  wait_vm<3 * kDmaPerStage>();
-  __syncthreads();
-  fload(0, wf[0], xf[0]);
-  sload(0, sc[0]);
-  wait_vm<2 * kDmaPerStage>();
-  __syncthreads();
-
-  // One K-step as 16 issue slots, each one MFMA followed by one fragment read for the next
+  // Step s: fragments of stage s are in registers [s & 1].  The step requests stage s + 4
+  // into the buffer stage s occupied (every wave read stage s's fragments during step s - 1,
+  // before the barrier that ended it) while it issues its 16 MFMAs and reads stage s + 1's
+  // fragments (and, on the last step of a superstep, the next superstep's exponents).  It
+  // ends by waiting for its own DMA of stage s + 2 (the two most recent DMA groups, of stages
+  // s + 3 and s + 4, may stay in flight) and a barrier, after which stage s + 2 is complete in
+  // LDS for all waves.  Each stage thus has three steps to arrive.
+  //
+  // One K-step is 16 issue slots, each one MFMA followed by one fragment read for the next
   // step and (in the first slots) one DMA request, separated by hard scheduling barriers: the
   // DMAs of the four wavefronts then trickle out one per MFMA instead of arriving at the
   // address unit as one burst after the barrier, and every MFMA has independent work behind it.
+  const int KS = a.KS;
   auto step = [&](auto q_c, int s, auto issue_c, auto wait_c) {
     constexpr int q = decltype(q_c)::value;        // step within the 256-K superstep
     constexpr int p = q & 1;
     constexpr bool do_issue = decltype(issue_c)::value;
     constexpr int nwait = decltype(wait_c)::value;
-    const int nb = (s + 1) & (kBufs - 1);          // buffer of stage s + 1
+    constexpr int nb = (q + 1) & (kBufs - 1);      // buffer of stage s + 1 (s % 4 == q)
     const int t = s + 4;                           // stage requested by this step
-    const uint32_t k_img = (uint32_t)t * kStageImage;
+    const uint8_t* const wsrc_t = wbase + (int64_t)t * kStageImage;
+    const uint8_t* const xsrc_t = xbase + (int64_t)t * kStageImage;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int cf = k >> 2, tf = k & 3;
@@ -257,13 +333,13 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
         if (k < 8) {
           const int i = k >> 1;
           if ((k & 1) == 0)
-            dma16(wdst + q * kStageImage + i * 1024, wsrc + k_img + i * 1024);
+            dma16_blk<q>(wdst, wsrc_t, kvoff16, i);
           else
-            dma16(xdst + q * kStageImage + i * 1024, xsrc + k_img + i * 1024);
+            dma16_blk<q>(xdst, xsrc_t, kvoff16, i);
         } else if (q == 0 && (k == 8 || k == 9)) {
           const int64_t sup = t >> 2;
           const uint32_t slot = sdst + (uint32_t)(sup & 1) * 2048;
-          dma4(slot + (k - 8) * 256, ssrc + sup * s_step + (k - 8) * 256);
+          dma4(slot + (k - 8) * 256, sbase + sup * s_step + (k - 8) * 256, kvoff16 >> 2);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -276,131 +352,181 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     if (nwait >= 0) wait_vm<(nwait < 0 ? 0 : nwait)>();
     __syncthreads();
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  using Yes = std::true_type;
-  using No = std::false_type;
-  using W40 = std::integral_constant<int, 2 * kDmaPerStage>;
-  using W20 = std::integral_constant<int, kDmaPerStage>;
-  using W0 = std::integral_constant<int, 0>;
-  using WN = std::integral_constant<int, -1>;
-  for (int s = 0; s < KS - 4; s += 4) {
-    step(I0{}, s, Yes{}, W40{});
-    step(I1{}, s + 1, Yes{}, W40{});
-    step(I2{}, s + 2, Yes{}, W40{});
-    step(I3{}, s + 3, Yes{}, W40{});
-  }
-  // last superstep: nothing left to request; the waits shrink with the groups in flight
-  step(I0{}, KS - 4, No{}, W20{});
-  step(I1{}, KS - 3, No{}, W0{});
-  step(I2{}, KS - 2, No{}, WN{});
-  step(I3{}, KS - 1, No{}, WN{});
 
-  // ---- epilogue ----
-  // x = acc * a_scale * c + bias (fp32) -> sums of squares from the fp32 values, bf16 into a
-  // per-wave 128 x 128 LDS tile (token rows of 256 bytes, 16-byte chunk j of row r at chunk
-  // position j ^ (r & 15), its two 8-byte halves swapped when bit 4 of r is set, so the 32
-  // rows of one 8-byte store phase hit distinct banks), then read back row-contiguous and
-  // stored as 16-byte vectors.
-  __builtin_amdgcn_sched_barrier(0);
-  uint8_t* const otile = (wm == 0 ? &lds_w[0][0] : &lds_x[0][0]) + wn * 32768;
-  // the epilogue's operands go to registers first, under one LDS wait: the row scales of this
-  // lane's 4 tokens and the bias (and channel scale) of its 16 channel quads
-  float sa[4];
-#pragma unroll
-  for (int tf = 0; tf < 4; ++tf) sa[tf] = lds_sa[wm * 128 + tf * 32 + fr];
-  float4 bq[4][4], cq[4][4];
-#pragma unroll
-  for (int cf = 0; cf < 4; ++cf)
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int cl = cf * 32 + rq * 8 + g * 4;
-      bq[cf][rq] = *reinterpret_cast<const float4*>(&lds_bias[wn * 128 + cl]);
-      if (kChanScale) cq[cf][rq] = *reinterpret_cast<const float4*>(&lds_cs[wn * 128 + cl]);
-    }
-  float sq_q[4] = {0.f, 0.f, 0.f, 0.f}, sq_k[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int cf = 0; cf < 4; ++cf) {
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int cl = cf * 32 + rq * 8 + g * 4;            // 4 consecutive channels (local)
-      const float bs[4] = {bq[cf][rq].x, bq[cf][rq].y, bq[cf][rq].z, bq[cf][rq].w};
-      float cs[4] = {1.f, 1.f, 1.f, 1.f};
-      if (kChanScale) {
-        cs[0] = cq[cf][rq].x; cs[1] = cq[cf][rq].y; cs[2] = cq[cf][rq].z; cs[3] = cq[cf][rq].w;
-      }
-      const int64_t ng = n0 + wn * 128 + cl;
-      // 0/1 masks of the Q and K segments (multiplies rather than branches keep the epilogue
-      // straight-line code)
-      const float mq = ng < a.Iq ? 1.f : 0.f;
-      const float mk = ng >= a.Iq && ng < a.Iq + a.Ik ? 1.f : 0.f;
-#pragma unroll
-      for (int tf = 0; tf < 4; ++tf) {
-        float x[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          x[e] = kChanScale ? acc[cf][tf][rq * 4 + e] * sa[tf] * cs[e] + bs[e]
-                            : fmaf(acc[cf][tf][rq * 4 + e], sa[tf], bs[e]);
-        const float s2 = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
-        sq_q[tf] = fmaf(mq, s2, sq_q[tf]);
-        sq_k[tf] = fmaf(mk, s2, sq_k[tf]);
-        const int row = tf * 32 + fr;
-        const int chunk = cf * 4 + rq;
-        u32x2_a8 o = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-        *reinterpret_cast<u32x2_a8*>(otile + row * 256 + ((chunk ^ (row & 15)) << 4) +
-                                     ((g ^ (row >> 4)) & 1) * 8) = o;
-      }
-    }
-  }
-  if (a.ws && n0 + wn * 128 < a.Iq + a.Ik) {        // this wave's channels overlap Q or K
-    const int64_t p = (int64_t)tn * 2 + wn;
-#pragma unroll
-    for (int tf = 0; tf < 4; ++tf) {
-      const float q = sq_q[tf] + __shfl_xor(sq_q[tf], 32);
-      const float k = sq_k[tf] + __shfl_xor(sq_k[tf], 32);
-      const int64_t tok = m0 + wm * 128 + tf * 32 + fr;
-      if (g == 0 && tok < a.T) {
-        u32x2_a8 o = {__float_as_uint(q), __float_as_uint(k)};
-        *reinterpret_cast<u32x2_a8*>(a.ws + (p * a.T + tok) * 2) = o;
-      }
-    }
-  }
-  // row-contiguous read-back: 16 lanes per 256-byte token row, 4 rows per instruction (rows
-  // 4 it .. 4 it + 3); eight LDS reads are in flight before their eight stores.  Streaming
+  // ---- epilogue of tile u (operands in buffer e), through stage buffer 3 ----
+  // x = acc * a_scale * c + bias (fp32) -> sums of squares from the fp32 values, bf16.  Four
+  // passes of 32 tokens: each wave packs its 32 x 128 bf16 block into an 8 KiB LDS area
+  // (token rows of 256 bytes, 16-byte chunk j of row r at chunk position j ^ (r & 15), its two
+  // 8-byte halves swapped when bit 4 of r is set, so the 32 rows of one 8-byte store phase hit
+  // distinct banks), reads it back row-contiguous (16 lanes per row, 4 rows per instruction,
+  // all eight reads in flight before their stores) and stores 16-byte vectors.  Streaming
   // (non-temporal) stores: the output is not re-read by this kernel, and keeping it out of L2
   // leaves L2 to the operand stage images that neighbouring tiles share.
-  const int jc = lane & 15;
-  const int64_t ch = n0 + wn * 128 + jc * 8;
-  const int64_t tok0 = m0 + wm * 128 + (lane >> 4);
-  uint16_t* const obase = a.out + tok0 * a.I + ch;
-  auto store_rows = [&](auto check_c) {
-    constexpr bool kCheck = decltype(check_c)::value;
+  auto epilogue = [&](Tile u, int e) {
+    // lane-derived addresses are recomputed here from a fresh lane index, so the compiler
+    // cannot hoist them out of the tile loop and keep them live through the K-steps
+    const int el = fresh_lane();
+    const int g = el >> 5, fr = el & 31;
+    uint8_t* const otile = (wm == 0 ? &lds_w[3][0] : &lds_x[3][0]) + wn * 8192;
+    const int64_t m0 = (int64_t)u.tm * kTileM, n0 = (int64_t)u.tn * kTileN;
+    const int jc = el & 15;
+    const int64_t ch = n0 + wn * 128 + jc * 8;
     const bool ch_ok = ch < a.I;
+    // the tile's output through a buffer descriptor whose range ends where the output array
+    // ends: stores to token rows >= T fall outside it and are dropped by the hardware's range
+    // check, so row bounds need no per-store predicate (in-tile offsets are < 256 * I * 2,
+    // which the host keeps below 2^31)
+    const int64_t out_left = ((a.T - m0) * a.I - n0) * 2;
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        a.out + m0 * a.I + n0, (short)0, (int)(uint32_t)min(out_left, (int64_t)0x7FFFFFFF),
+        kBufferRsrcWord3);
+    const uint32_t row_bytes = (uint32_t)a.I * 2;
+    const uint32_t lane_off = (uint32_t)(wm * 128 + (el >> 4)) * row_bytes + (uint32_t)(wn * 128 + jc * 8) * 2;
+    float sq_q[4] = {0.f, 0.f, 0.f, 0.f}, sq_k[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int b8 = 0; b8 < 4; ++b8) {
+    for (int tf = 0; tf < 4; ++tf) {
+      // this pass's operands to registers first, under one LDS wait: the row scale of this
+      // lane's token and the bias (and channel scale) of its 16 channel quads
+      const float sa = lds_sa[e][wm * 128 + tf * 32 + fr];
+      float4 bq[4][4], cq[4][4];
+#pragma unroll
+      for (int cf = 0; cf < 4; ++cf)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int cl = cf * 32 + rq * 8 + g * 4;
+          bq[cf][rq] = *reinterpret_cast<const float4*>(&lds_bias[e][wn * 128 + cl]);
+          if (kChanScale) cq[cf][rq] = *reinterpret_cast<const float4*>(&lds_cs[e][wn * 128 + cl]);
+        }
+#pragma unroll
+      for (int cf = 0; cf < 4; ++cf) {
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int cl = cf * 32 + rq * 8 + g * 4;        // 4 consecutive channels (local)
+          const float bs[4] = {bq[cf][rq].x, bq[cf][rq].y, bq[cf][rq].z, bq[cf][rq].w};
+          float cs[4] = {1.f, 1.f, 1.f, 1.f};
+          if (kChanScale) {
+            cs[0] = cq[cf][rq].x; cs[1] = cq[cf][rq].y; cs[2] = cq[cf][rq].z; cs[3] = cq[cf][rq].w;
+          }
+          // 0/1 masks of the Q and K segments (multiplies rather than branches keep the
+          // epilogue straight-line code); segment boundaries are multiples of 16 channels, so
+          // the 8-channel group cf * 32 + rq * 8 lies in one segment and the masks are
+          // wave-uniform
+          const int64_t ng8 = n0 + wn * 128 + cf * 32 + rq * 8;
+          const float mq = ng8 < a.Iq ? 1.f : 0.f;
+          const float mk = ng8 >= a.Iq && ng8 < a.Iq + a.Ik ? 1.f : 0.f;
+          float x[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            x[i] = kChanScale ? acc[cf][tf][rq * 4 + i] * sa * cs[i] + bs[i]
+                              : fmaf(acc[cf][tf][rq * 4 + i], sa, bs[i]);
+          const float s2 = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+          sq_q[tf] = fmaf(mq, s2, sq_q[tf]);
+          sq_k[tf] = fmaf(mk, s2, sq_k[tf]);
+          const int chunk = cf * 4 + rq;
+          u32x2_a8 o = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+          *reinterpret_cast<u32x2_a8*>(otile + fr * 256 + ((chunk ^ (fr & 15)) << 4) +
+                                       ((g ^ (fr >> 4)) & 1) * 8) = o;
+        }
+      }
+      const uint32_t obyte = lane_off + (uint32_t)(tf * 32) * row_bytes;
       uint4 v[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int row = (b8 * 8 + j) * 4 + (lane >> 4);
+        const int row = j * 4 + (el >> 4);
         v[j] = *reinterpret_cast<const uint4*>(otile + row * 256 + ((jc ^ (row & 15)) << 4));
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int it = b8 * 8 + j;
-        // bit 4 of the row is bit 2 of it: those rows hold their 8-byte halves swapped
-        const u32x4 o = ((it >> 2) & 1) ? u32x4{v[j].z, v[j].w, v[j].x, v[j].y}
-                                        : u32x4{v[j].x, v[j].y, v[j].z, v[j].w};
-        if (!kCheck || (ch_ok && tok0 + it * 4 < a.T))
-          __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(obase + (int64_t)it * 4 * a.I));
+        // bit 4 of the row is bit 2 of j: those rows hold their 8-byte halves swapped
+        const u32x4 o = ((j >> 2) & 1) ? u32x4{v[j].z, v[j].w, v[j].x, v[j].y}
+                                       : u32x4{v[j].x, v[j].y, v[j].z, v[j].w};
+        if (ch_ok)
+          __builtin_amdgcn_raw_buffer_store_b128(o, orsrc, (int)(obyte + (uint32_t)(j * 4) * row_bytes),
+                                                 0, kNonTemporal);
+      }
+      __builtin_amdgcn_sched_barrier(0);      // passes stay in order: bounded register use
+    }
+    if (a.ws && n0 + wn * 128 < a.Iq + a.Ik) {      // this wave's channels overlap Q or K
+      const int64_t p = (int64_t)u.tn * 2 + wn;
+#pragma unroll
+      for (int tf = 0; tf < 4; ++tf) {
+        const float q = add_xor32(sq_q[tf]);
+        const float k = add_xor32(sq_k[tf]);
+        const int64_t tok = m0 + wm * 128 + tf * 32 + fr;
+        if (g == 0 && tok < a.T) {
+          u32x2_a8 o = {__float_as_uint(q), __float_as_uint(k)};
+          *reinterpret_cast<u32x2_a8*>(a.ws + (p * a.T + tok) * 2) = o;
+        }
       }
     }
   };
-  if (m0 + kTileM <= a.T && n0 + kTileN <= a.I)      // whole tile inside the output
-    store_rows(std::false_type{});
-  else
-    store_rows(std::true_type{});
+
+  // ---- tile loop ----
+  // Before the first tile: its stages 0-2 and epilogue operands requested.  Each tile then:
+  // waits for everything in flight (stages 0-2 and operands of this tile, the previous tile's
+  // output stores), barrier (stage buffer 3, the previous epilogue's staging area, is free;
+  // stages 0-2 and the operands are visible), requests stage 3, widens the bias, reads stage
+  // 0's fragments, barrier, runs the K-steps.  After the last K-step it requests stages 0-2
+  // and the epilogue operands of its next tile, which arrive while this tile's epilogue runs.
+  issue(I0{}, 0);
+  issue(I1{}, 1);
+  issue(I2{}, 2);
+  issue_ops(t, 0);
+  int e = 0;
+  for (;;) {
+    wait_vm<0>();
+    __syncthreads();
+    issue(I3{}, 3);
+    {
+      const int lt = wave * 64 + fresh_lane();
+      const uint32_t w = lds_braw[e][lt >> 1];
+      lds_bias[e][lt] = a.bias ? bf16_to_f32((lt & 1) ? w >> 16 : w & 0xFFFFu) : 0.0f;
+    }
+    set_lane_offsets();
+#pragma unroll
+    for (int cf = 0; cf < 4; ++cf)
+#pragma unroll
+      for (int tf = 0; tf < 4; ++tf)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[cf][tf][r] = 0.0f;
+    fload(0, wf[0], xf[0]);
+    sload(0, sc[0]);
+    __syncthreads();
+    for (int s = 0; s < KS - 4; s += 4) {
+      step(I0{}, s, Yes{}, W40{});
+      step(I1{}, s + 1, Yes{}, W40{});
+      step(I2{}, s + 2, Yes{}, W40{});
+      step(I3{}, s + 3, Yes{}, W40{});
+    }
+    // last superstep: nothing left to request; the waits shrink with the groups in flight
+    step(I0{}, KS - 4, No{}, W20{});
+    step(I1{}, KS - 3, No{}, W0{});
+    step(I2{}, KS - 2, No{}, WN{});
+    step(I3{}, KS - 1, No{}, WN{});
+    // pin the accumulators here: without this the compiler sinks the last superstep's MFMAs
+    // (their results are only read by the epilogue) below the next tile's DMA requests
+#pragma unroll
+    for (int cf = 0; cf < 4; ++cf)
+#pragma unroll
+      for (int tf = 0; tf < 4; ++tf) asm volatile("" : "+a"(acc[cf][tf]));
+    __builtin_amdgcn_sched_barrier(0);
+
+    const Tile cur = t;
+    const bool more = k_in + xcd_blocks < xcd_count;
+    if (more) {
+      k_in += xcd_blocks;
+      t = decode_tile(xcd_first + k_in, a.tiles_m, a.tiles_n);
+      set_sources(t);
+      issue(I0{}, 0);
+      issue(I1{}, 1);
+      issue(I2{}, 2);
+      issue_ops(t, e ^ 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    epilogue(cur, e);
+    if (!more) break;
+    e ^= 1;
+  }
 }
 
 // Activation codes [T, stride] (rows only 4-byte aligned in the packed [T, H + 4] layout) ->
@@ -462,7 +588,14 @@ hipError_t launch_project(const uint8_t* a_codes, int64_t a_stride, const uint8_
   hipLaunchKernelGGL(act_repack_kernel, rg, dim3(256), 0, s, a_codes, a_stride, T, H, a.KS, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned nblocks = (unsigned)(a.tiles_m * a.tiles_n);
+  // persistent blocks: one per compute unit (the kernel's LDS admits one block per CU), each
+  // walking its XCD's tile range
+  int dev = 0, cus = 0;
+  e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n;
+  const unsigned nblocks = (unsigned)std::min<int64_t>(ntiles, std::max(cus, 1));
   if (chan_scale)
     hipLaunchKernelGGL(project_kernel<true>, dim3(nblocks), dim3(kThreads), 0, s, a);
   else

@@ -132,6 +132,8 @@ qkvmx_status qkv_rowmx_project(const uint8_t* a_codes, int64_t a_row_stride,
   const int64_t I = (int64_t)(num_heads + 2 * (int64_t)num_kv_heads) * head_dim;
   if ((T - 1) * a_row_stride + H >= kMaxOffset)
     return fail(QKVMX_ERR_UNSUPPORTED, "qkv_rowmx_project: activation span must be < 2^31 bytes");
+  if (I * 2 * 256 >= kMaxOffset)     // byte offsets within one 256-token output tile
+    return fail(QKVMX_ERR_UNSUPPORTED, "qkv_rowmx_project: I must be < 2^22");
   if (ws_bytes < workspace_total_bytes(T, H, I))
     return fail(QKVMX_ERR_WORKSPACE, "qkv_rowmx_project: workspace %zu < %zu bytes", ws_bytes, workspace_total_bytes(T, H, I));
   if (!aligned(a_codes, 4) || !aligned(a_scales, 4) || !aligned(w_packed, 256) ||
