@@ -62,6 +62,64 @@ def copy_calibration(nbytes: int):
     print(json.dumps({"copy_bytes": nbytes, "launches": 3}), flush=True)
 
 
+PROJECTION_KERNELS = ("act_repack_kernel", "project_kernel", "ssq_reduce_kernel")
+
+
+def _counter_means(run_dir: str, counter: str):
+    """Mean value of `counter` per dispatch, per kernel name, from a rocprofv3 --pmc CSV run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    acc = {}
+    for f in files:
+        for row in csv.DictReader(open(f)):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"].replace("(anonymous namespace)::", "")
+            name = name.split("(")[0].split("<")[0].split("::")[-1].split()[-1]
+            key = (name, row["Dispatch_Id"])
+            acc[key] = acc.get(key, 0.0) + float(row["Counter_Value"])
+    per = {}
+    for (name, _), v in acc.items():
+        per.setdefault(name, []).append(v)
+    return {k: sum(v) / len(v) for k, v in per.items()}
+
+
+def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes):
+    """Scaled HBM bytes per projection call from four rocprofv3 --pmc runs (FETCH_SIZE and
+    WRITE_SIZE of the benchmark, the same two of a plain copy of copy_bytes bytes, which give
+    the counters' scale), written to the traffic record the benchmark line reports."""
+    import synth
+    p = synth.CONFIGS[5].calls[0]
+    copy_kib = copy_bytes / 1024.0
+    cf = _counter_means(copy_fetch_dir, "FETCH_SIZE")
+    cw = _counter_means(copy_write_dir, "WRITE_SIZE")
+    ck = max(cf, key=cf.get)                       # the copy kernel: the largest dispatch
+    fetch_scale, write_scale = copy_kib / cf[ck], copy_kib / cw[ck]
+    fk, wk = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
+    T, H, I = p.T, p.H, p.I
+    alg = {"act_repack_kernel": (T * H, T * H),
+           "project_kernel": (T * H + H * I + T * 4, 2 * T * I),
+           "ssq_reduce_kernel": (4 * T * 2 * ((p.Iq + p.Ik) // 128), 8 * T)}
+    per = {}
+    for k in PROJECTION_KERNELS:
+        per[k] = {"fetch_kib": fk[k], "write_kib": wk[k],
+                  "read_bytes": fk[k] * 1024 * fetch_scale, "write_bytes": wk[k] * 1024 * write_scale,
+                  "alg_read_bytes": alg[k][0], "alg_write_bytes": alg[k][1]}
+    rec = {"what": f"HBM bytes per qkv_rowmx_project launch ({' + '.join(PROJECTION_KERNELS)}) at "
+                   f"T={T} H={H} I={I}, from rocprofv3 FETCH_SIZE/WRITE_SIZE scaled by a "
+                   f"{copy_bytes}-byte copy calibration (copy kernel {ck})",
+           "kernel_src_sha256_16": source_digest(PROJECT_SRC),
+           "fetch_scale": fetch_scale, "write_scale": write_scale, "per_kernel": per,
+           "hbm_bytes_per_launch": sum(v["read_bytes"] + v["write_bytes"] for v in per.values())}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps({"traffic_file": TRAFFIC_FILE, "hbm_bytes_per_launch": rec["hbm_bytes_per_launch"],
+                      "fetch_scale": fetch_scale, "write_scale": write_scale}))
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -72,6 +130,11 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
+                                                             "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="only write the traffic record from four rocprofv3 --pmc runs (no GPU)")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30,
+                    help="size of the calibration copy the --summarize-traffic runs used")
     return ap.parse_args()
 
 
@@ -242,6 +305,9 @@ def cpu_baseline(cid, rows_n):
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.copy_bytes)
+        return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return

@@ -2,7 +2,9 @@
 
 Every HIP source is compiled with packed-fp32 instruction forms disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the compiler still schedules ordinary
-fp32 code.  Object files go to ``_build/`` next to this file and the shared library next to the
+fp32 code.  The wave-level atomic rewrite is switched off
+(``-amdgpu-atomic-optimizer-strategy=None``): the projection's tile-counter atomic is issued by
+one lane and must not have its result read back at the point of issue.  Object files go to ``_build/`` next to this file and the shared library next to the
 package sources, where the Python binding loads it.
 """
 from __future__ import annotations
@@ -24,6 +26,7 @@ ARCH = "gfx950"
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function",
     f"-I{os.path.join(ROOT, 'include')}",
 ]

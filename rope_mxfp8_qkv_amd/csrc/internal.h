@@ -50,12 +50,20 @@ inline size_t packed_total_bytes(int64_t H, int64_t I) {
 }
 inline int64_t ssq_partials(int64_t I) { return ceil_div(I, kTileN) * (kTileN / kPartialN); }
 // Projection workspace: the activation codes re-laid as stage images [MT][KS][16 KiB]
-// (MT = ceil(T / 256) token tiles), then the sum-of-squares partials [P][T][2] fp32.
+// (MT = ceil(T / 256) token tiles), then the sum-of-squares partials [P][T][2] fp32, then a
+// 256-byte block holding the per-XCD tile counters of the projection's tile scheduler.
 inline size_t act_image_bytes(int64_t T, int64_t H) {
   return (size_t)ceil_div(T, kTileM) * packed_stages(H) * kStageImage;
 }
+inline size_t partials_bytes(int64_t T, int64_t I) {
+  return (size_t)ssq_partials(I) * (size_t)T * 2 * sizeof(float);
+}
+constexpr size_t kCounterBytes = 256;
+inline size_t counters_offset(int64_t T, int64_t H, int64_t I) {
+  return (act_image_bytes(T, H) + partials_bytes(T, I) + 255) / 256 * 256;
+}
 inline size_t workspace_total_bytes(int64_t T, int64_t H, int64_t I) {
-  return act_image_bytes(T, H) + (size_t)ssq_partials(I) * (size_t)T * 2 * sizeof(float);
+  return counters_offset(T, H, I) + kCounterBytes;
 }
 
 hipError_t launch_mx_weight_quantize(const float* w, int64_t H, int64_t I, uint8_t* codes,

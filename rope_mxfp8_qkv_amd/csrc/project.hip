@@ -30,9 +30,12 @@
 //    (groups holding only V write none), bf16 round-to-nearest-even (V_CVT_PK_BF16_F32),
 //    transposed through LDS so every global store is a coalesced 16-byte vector along a token
 //    row.  A small second kernel adds the partials in a fixed order (deterministic, no atomics).
-//  * Tile order: block ids are dealt round-robin to the 8 XCDs; they are remapped so that each
-//    XCD owns a contiguous range of tiles, walked in groups of 8 token tiles x all channel tiles,
-//    so the tiles resident on one XCD share activation rows and weight columns in its L2.
+//  * Tile order and scheduling: one persistent block per CU.  The tiles are split into 8
+//    contiguous ranges, one per XCD, walked in groups of 8 token tiles x all channel tiles;
+//    a block claims tiles one at a time from its own XCD's range (an atomic counter), so the
+//    tiles resident on one XCD at any time share activation rows and weight columns in its
+//    L2, and it prefetches the next tile's first stages while the current tile's epilogue
+//    runs.
 #include <algorithm>
 #include <type_traits>
 
@@ -52,6 +55,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;                         // token tiles per raster group
 constexpr int kXcds = 8;
+constexpr int kHwRegXccId = 20 | (31 << 11);        // s_getreg operand: XCC_ID, bits [31:0]
 constexpr int kBufs = 4;                           // LDS stage buffers
 constexpr int kBufferRsrcWord3 = 0x00020000;        // buffer descriptor word 3 (gfx9 family)
 constexpr int kNonTemporal = 2;                    // buffer store cache policy: streaming
@@ -73,6 +77,7 @@ struct ProjectArgs {
   int tiles_m, tiles_n;
   uint16_t* out;
   float* ws;                   // [P][T][2] or null
+  unsigned* ctr;               // [8] tile counters, one per XCD (zeroed by the repack kernel)
 };
 
 __device__ __forceinline__ int lds_off(int row, int chunk) {
@@ -151,7 +156,7 @@ __device__ __forceinline__ Tile decode_tile(int tile, int tiles_m, int tiles_n) 
   return Tile{first_m + in_group % gm, in_group / gm};
 }
 
-template <bool kChanScale>
+template <bool kChanScale, bool kBias>
 __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_w[kBufs][kStageImage];
   __shared__ __attribute__((aligned(16))) uint8_t lds_x[kBufs][kStageImage];
@@ -170,17 +175,36 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   const int wn = wave & 1;        // channel half of the block tile
   const int wm = wave >> 1;       // token half
 
-  // ---- tiles of this block: XCD-contiguous ranges, visited with a stride of the XCD's blocks
+  // ---- tile scheduler ----
+  // The tiles are split into 8 contiguous ranges, one per XCD (grouped raster order inside
+  // each).  A block claims its tiles one at a time from the counter of the XCD it runs on
+  // (read from the XCC_ID register), so the tiles in flight on an XCD always form a compact
+  // window that shares operand stage images in that XCD's L2; once that range is used up it
+  // takes tiles from the other XCDs' ranges.  Thread 0 claims; the tile id reaches the block
+  // through LDS.
+  __shared__ int lds_tile[2];
+  __shared__ unsigned lds_ticket;
   const int ntiles = a.tiles_m * a.tiles_n;
-  const int b = blockIdx.x;
-  const int xcd = b % kXcds;
   const int per = ntiles / kXcds, rem = ntiles % kXcds;
-  const int xcd_first = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
-  const int xcd_count = per + (xcd < rem ? 1 : 0);
-  const int xcd_blocks = ((int)gridDim.x - xcd + kXcds - 1) / kXcds;
-  int k_in = b / kXcds;
-  if (k_in >= xcd_count) return;          // the whole block, before any barrier
-  Tile t = decode_tile(xcd_first + k_in, a.tiles_m, a.tiles_n);
+  const int my_xcd = __builtin_amdgcn_s_getreg(kHwRegXccId) & (kXcds - 1);
+  auto range_first = [&](int x) { return x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per; };
+  auto range_count = [&](int x) { return per + (x < rem ? 1 : 0); };
+  // tile for ticket k of this XCD's counter, else the first one left in another range (-1:
+  // none left anywhere); thread 0 only
+  auto claim = [&](int k) -> int {
+    if (k < range_count(my_xcd)) return range_first(my_xcd) + k;
+    for (int d = 1; d < kXcds; ++d) {
+      const int x = (my_xcd + d) & (kXcds - 1);
+      const int kx = (int)atomicAdd(&a.ctr[x], 1u);
+      if (kx < range_count(x)) return range_first(x) + kx;
+    }
+    return -1;
+  };
+  if (tid == 0) lds_tile[0] = claim((int)atomicAdd(&a.ctr[my_xcd], 1u));
+  __syncthreads();
+  const int first_tile = __builtin_amdgcn_readfirstlane(lds_tile[0]);
+  if (first_tile < 0) return;             // the whole block, nothing left
+  Tile t = decode_tile(first_tile, a.tiles_m, a.tiles_n);
 
   // ---- DMA sources of the current tile (wave-uniform bases, in SGPRs) ----
   // weight: wave w copies 1 KiB blocks 4 w .. 4 w + 3 of each 16 KiB stage image;
@@ -202,7 +226,7 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
 
   // DMA of stage t (t % 4 == Q) into buffer Q; a stage opening a superstep also brings that
   // superstep's exponents into ring slot (t / 4) % 2.
-  auto issue = [&](auto q_c, int t) {
+  auto issue = [&](auto q_c, int t) __attribute__((always_inline)) {
     constexpr int Q = decltype(q_c)::value;
     const uint32_t lv = fresh_lane();
     const uint32_t voff16 = lv * 16, voff4 = lv * 4;
@@ -233,7 +257,7 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
       const int64_t n = min((int64_t)u.tn * kTileN + wave * 64 + lv, a.I - 1);
       dma4g(lds_addr(&lds_cs[e][wave * 64]), a.chan_scale + n);
     }
-    if (a.bias && wave < 2) {
+    if (kBias && wave < 2) {
       const int64_t n2 = min((int64_t)u.tn * kTileN + 2 * (wave * 64 + lv), a.I - 2);
       dma4g(lds_addr(&lds_braw[e][wave * 64]), a.bias + n2);
     }
@@ -304,7 +328,7 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   // DMAs of the four wavefronts then trickle out one per MFMA instead of arriving at the
   // address unit as one burst after the barrier, and every MFMA has independent work behind it.
   const int KS = a.KS;
-  auto step = [&](auto q_c, int s, auto issue_c, auto wait_c) {
+  auto step = [&](auto q_c, int s, auto issue_c, auto wait_c) __attribute__((always_inline)) {
     constexpr int q = decltype(q_c)::value;        // step within the 256-K superstep
     constexpr int p = q & 1;
     constexpr bool do_issue = decltype(issue_c)::value;
@@ -362,7 +386,7 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   // all eight reads in flight before their stores) and stores 16-byte vectors.  Streaming
   // (non-temporal) stores: the output is not re-read by this kernel, and keeping it out of L2
   // leaves L2 to the operand stage images that neighbouring tiles share.
-  auto epilogue = [&](Tile u, int e) {
+  auto epilogue = [&](Tile u, int e) __attribute__((always_inline)) {
     // lane-derived addresses are recomputed here from a fresh lane index, so the compiler
     // cannot hoist them out of the tile loop and keep them live through the K-steps
     const int el = fresh_lane();
@@ -462,25 +486,34 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   };
 
   // ---- tile loop ----
-  // Before the first tile: its stages 0-2 and epilogue operands requested.  Each tile then:
-  // waits for everything in flight (stages 0-2 and operands of this tile, the previous tile's
-  // output stores), barrier (stage buffer 3, the previous epilogue's staging area, is free;
-  // stages 0-2 and the operands are visible), requests stage 3, widens the bias, reads stage
-  // 0's fragments, barrier, runs the K-steps.  After the last K-step it requests stages 0-2
-  // and the epilogue operands of its next tile, which arrive while this tile's epilogue runs.
+  // Before the first tile: its stages 0-2 and epilogue operands requested, and a ticket for
+  // the following tile drawn.  Each tile then: waits for everything in flight (stages 0-2 and
+  // operands of this tile, the previous tile's output stores, the ticket), turns the ticket
+  // into the next tile's id (thread 0, into LDS slot e ^ 1), barrier (stage buffer 3, the
+  // previous epilogue's staging area, is free; stages 0-2, the operands and the next tile's id
+  // are visible), requests stage 3, widens the bias, reads stage 0's fragments, barrier, runs
+  // the K-steps.  After the last K-step it requests stages 0-2 and the epilogue operands of
+  // the next tile, which arrive while this tile's epilogue runs, and it draws the ticket after
+  // its output stores (waiting for the atomic there overlaps the stores' drain).
   issue(I0{}, 0);
   issue(I1{}, 1);
   issue(I2{}, 2);
   issue_ops(t, 0);
-  int e = 0;
-  for (;;) {
+  // thread 0 only: a ticket of this XCD's counter, kept in LDS (no register carries it round
+  // the loop)
+  if (tid == 0) lds_ticket = atomicAdd(&a.ctr[my_xcd], 1u);
+  // the tile body, instantiated for operand buffer e = 0 and e = 1 (tiles alternate), so the
+  // buffer index is a constant everywhere; returns whether another tile follows
+  auto tile_iter = [&](auto e_c) __attribute__((always_inline)) -> bool {
+    constexpr int e = decltype(e_c)::value;
     wait_vm<0>();
+    if (tid == 0) lds_tile[e ^ 1] = claim((int)lds_ticket);
     __syncthreads();
     issue(I3{}, 3);
     {
       const int lt = wave * 64 + fresh_lane();
       const uint32_t w = lds_braw[e][lt >> 1];
-      lds_bias[e][lt] = a.bias ? bf16_to_f32((lt & 1) ? w >> 16 : w & 0xFFFFu) : 0.0f;
+      lds_bias[e][lt] = kBias ? bf16_to_f32((lt & 1) ? w >> 16 : w & 0xFFFFu) : 0.0f;
     }
     set_lane_offsets();
 #pragma unroll
@@ -492,7 +525,11 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     fload(0, wf[0], xf[0]);
     sload(0, sc[0]);
     __syncthreads();
-    for (int s = 0; s < KS - 4; s += 4) {
+    // the trip count is re-read through an opaque copy each tile: a loop-invariant test hoisted
+    // out of the tile loop would be kept in a register (or spilled) across the whole tile
+    int ks_opaque = KS;
+    asm volatile("" : "+s"(ks_opaque));
+    for (int s = 0; s < ks_opaque - 4; s += 4) {
       step(I0{}, s, Yes{}, W40{});
       step(I1{}, s + 1, Yes{}, W40{});
       step(I2{}, s + 2, Yes{}, W40{});
@@ -512,10 +549,10 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     __builtin_amdgcn_sched_barrier(0);
 
     const Tile cur = t;
-    const bool more = k_in + xcd_blocks < xcd_count;
+    const int next_tile = __builtin_amdgcn_readfirstlane(lds_tile[e ^ 1]);
+    const bool more = next_tile >= 0;
     if (more) {
-      k_in += xcd_blocks;
-      t = decode_tile(xcd_first + k_in, a.tiles_m, a.tiles_n);
+      t = decode_tile(next_tile, a.tiles_m, a.tiles_n);
       set_sources(t);
       issue(I0{}, 0);
       issue(I1{}, 1);
@@ -524,8 +561,13 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     }
     __builtin_amdgcn_sched_barrier(0);
     epilogue(cur, e);
-    if (!more) break;
-    e ^= 1;
+    if (!more) return false;
+    if (tid == 0) lds_ticket = atomicAdd(&a.ctr[my_xcd], 1u);
+    return true;
+  };
+  for (;;) {
+    if (!tile_iter(std::integral_constant<int, 0>{})) break;
+    if (!tile_iter(std::integral_constant<int, 1>{})) break;
   }
 }
 
@@ -535,7 +577,11 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
 // One thread per 16-byte position.
 __global__ void __launch_bounds__(256) act_repack_kernel(const uint8_t* __restrict__ a,
                                                          int64_t stride, int64_t T, int64_t H,
-                                                         int KS, uint8_t* __restrict__ img) {
+                                                         int KS, uint8_t* __restrict__ img,
+                                                         unsigned* __restrict__ ctr) {
+  // this kernel runs before every projection launch: it also resets the tile counters
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < kXcds)
+    ctr[threadIdx.x] = 0;
   const int p = blockIdx.x * blockDim.x + threadIdx.x;   // 0..1023
   const int64_t t = blockIdx.y;
   const int64_t tm = blockIdx.z;
@@ -585,7 +631,9 @@ hipError_t launch_project(const uint8_t* a_codes, int64_t a_stride, const uint8_
   float* partials = reinterpret_cast<float*>(ws + act_image_bytes(T, H));
   a.ws = ssq ? partials : nullptr;
   dim3 rg(kStageImage / 16 / 256, (unsigned)a.KS, (unsigned)a.tiles_m);
-  hipLaunchKernelGGL(act_repack_kernel, rg, dim3(256), 0, s, a_codes, a_stride, T, H, a.KS, ws);
+  a.ctr = reinterpret_cast<unsigned*>(ws + counters_offset(T, H, I));
+  hipLaunchKernelGGL(act_repack_kernel, rg, dim3(256), 0, s, a_codes, a_stride, T, H, a.KS, ws,
+                     a.ctr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // persistent blocks: one per compute unit (the kernel's LDS admits one block per CU), each
@@ -596,10 +644,15 @@ hipError_t launch_project(const uint8_t* a_codes, int64_t a_stride, const uint8_
   if (e != hipSuccess) return e;
   const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n;
   const unsigned nblocks = (unsigned)std::min<int64_t>(ntiles, std::max(cus, 1));
-  if (chan_scale)
-    hipLaunchKernelGGL(project_kernel<true>, dim3(nblocks), dim3(kThreads), 0, s, a);
+  const dim3 grid(nblocks), block(kThreads);
+  if (chan_scale && bias)
+    hipLaunchKernelGGL((project_kernel<true, true>), grid, block, 0, s, a);
+  else if (chan_scale)
+    hipLaunchKernelGGL((project_kernel<true, false>), grid, block, 0, s, a);
+  else if (bias)
+    hipLaunchKernelGGL((project_kernel<false, true>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL(project_kernel<false>, dim3(nblocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((project_kernel<false, false>), grid, block, 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess || !ssq) return e;
   // only the partials of 128-channel groups that overlap Q or K are written and summed

@@ -49,7 +49,7 @@ def test_size_queries():
     assert L.qkv_weight_packed_bytes(5120, 15360) >= 5120 * 15360 + 15360 * 20 * 8
     assert L.qkv_weight_packed_bytes(100, 16) == 0           # H % 32 != 0
     # activation stage images (296 token tiles x 80 stages x 16 KiB) + 120 partials per token
-    assert L.qkvmx_workspace_bytes(75600, 5120, 15360) == 296 * 80 * 16384 + 120 * 75600 * 8
+    assert L.qkvmx_workspace_bytes(75600, 5120, 15360) == 296 * 80 * 16384 + 120 * 75600 * 8 + 256
     assert L.qkvmx_workspace_bytes(0, 256, 16) == 0
     assert L.qkvmx_workspace_bytes(4, 100, 16) == 0
 
