@@ -273,6 +273,8 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   using W20 = std::integral_constant<int, kDmaPerStage>;
   using W0 = std::integral_constant<int, 0>;
   using WN = std::integral_constant<int, -1>;
+  using Z = std::true_type;                       // step starts the accumulators from zero
+  using NZ = std::false_type;
 
   // lane-derived LDS offsets of the K-steps, recomputed at the start of every tile (from a
   // fresh lane index) so that none of them is live across the epilogue
@@ -328,8 +330,10 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   // DMAs of the four wavefronts then trickle out one per MFMA instead of arriving at the
   // address unit as one burst after the barrier, and every MFMA has independent work behind it.
   const int KS = a.KS;
-  auto step = [&](auto q_c, int s, auto issue_c, auto wait_c) __attribute__((always_inline)) {
+  auto step = [&](auto q_c, int s, auto issue_c, auto wait_c, auto zero_c)
+                  __attribute__((always_inline)) {
     constexpr int q = decltype(q_c)::value;        // step within the 256-K superstep
+    constexpr bool from_zero = decltype(zero_c)::value;   // first K-step: accumulators start at 0
     constexpr int p = q & 1;
     constexpr bool do_issue = decltype(issue_c)::value;
     constexpr int nwait = decltype(wait_c)::value;
@@ -341,7 +345,8 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     for (int k = 0; k < 16; ++k) {
       const int cf = k >> 2, tf = k & 3;
       acc[cf][tf] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          wf[p][cf], xf[p][tf], acc[cf][tf], 0, 0, q, (int)sc[0][cf], 0, 0x7F7F7F7F);
+          wf[p][cf], xf[p][tf], from_zero ? v16f{} : acc[cf][tf], 0, 0, q, (int)sc[0][cf], 0,
+          0x7F7F7F7F);
       // fragment k / 2 of stage s + 1: even k -> weight fragment, odd k -> activation fragment
       const int f = k >> 2, half = (k >> 1) & 1;
       if ((k & 1) == 0) {
@@ -516,12 +521,6 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
       lds_bias[e][lt] = kBias ? bf16_to_f32((lt & 1) ? w >> 16 : w & 0xFFFFu) : 0.0f;
     }
     set_lane_offsets();
-#pragma unroll
-    for (int cf = 0; cf < 4; ++cf)
-#pragma unroll
-      for (int tf = 0; tf < 4; ++tf)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[cf][tf][r] = 0.0f;
     fload(0, wf[0], xf[0]);
     sload(0, sc[0]);
     __syncthreads();
@@ -529,17 +528,26 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     // out of the tile loop would be kept in a register (or spilled) across the whole tile
     int ks_opaque = KS;
     asm volatile("" : "+s"(ks_opaque));
-    for (int s = 0; s < ks_opaque - 4; s += 4) {
-      step(I0{}, s, Yes{}, W40{});
-      step(I1{}, s + 1, Yes{}, W40{});
-      step(I2{}, s + 2, Yes{}, W40{});
-      step(I3{}, s + 3, Yes{}, W40{});
+    // K-step 0 feeds zero accumulators to its MFMAs (no separate clearing of the 256 AGPRs)
+    if (ks_opaque > 4) {
+      step(I0{}, 0, Yes{}, W40{}, Z{});
+      step(I1{}, 1, Yes{}, W40{}, NZ{});
+      step(I2{}, 2, Yes{}, W40{}, NZ{});
+      step(I3{}, 3, Yes{}, W40{}, NZ{});
+      for (int s = 4; s < ks_opaque - 4; s += 4) {
+        step(I0{}, s, Yes{}, W40{}, NZ{});
+        step(I1{}, s + 1, Yes{}, W40{}, NZ{});
+        step(I2{}, s + 2, Yes{}, W40{}, NZ{});
+        step(I3{}, s + 3, Yes{}, W40{}, NZ{});
+      }
+      // last superstep: nothing left to request; the waits shrink with the groups in flight
+      step(I0{}, KS - 4, No{}, W20{}, NZ{});
+    } else {
+      step(I0{}, 0, No{}, W20{}, Z{});             // one superstep only
     }
-    // last superstep: nothing left to request; the waits shrink with the groups in flight
-    step(I0{}, KS - 4, No{}, W20{});
-    step(I1{}, KS - 3, No{}, W0{});
-    step(I2{}, KS - 2, No{}, WN{});
-    step(I3{}, KS - 1, No{}, WN{});
+    step(I1{}, KS - 3, No{}, W0{}, NZ{});
+    step(I2{}, KS - 2, No{}, WN{}, NZ{});
+    step(I3{}, KS - 1, No{}, WN{}, NZ{});
     // pin the accumulators here: without this the compiler sinks the last superstep's MFMAs
     // (their results are only read by the epilogue) below the next tile's DMA requests
 #pragma unroll
