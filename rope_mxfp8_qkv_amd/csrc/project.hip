@@ -412,37 +412,39 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     const uint32_t row_bytes = (uint32_t)a.I * 2;
     const uint32_t lane_off = (uint32_t)(wm * 128 + (el >> 4)) * row_bytes + (uint32_t)(wn * 128 + jc * 8) * 2;
     float sq_q[4] = {0.f, 0.f, 0.f, 0.f}, sq_k[4] = {0.f, 0.f, 0.f, 0.f};
+    // number of this wave's 8-channel groups (of 16) inside Q, and inside Q or K (uniform)
+    const int64_t c0 = n0 + wn * 128;
+    const int gq = __builtin_amdgcn_readfirstlane((int)min(max((a.Iq - c0) / 8, (int64_t)0), (int64_t)16));
+    const int gqk = __builtin_amdgcn_readfirstlane((int)min(max((a.Iq + a.Ik - c0) / 8, (int64_t)0), (int64_t)16));
 #pragma unroll
     for (int tf = 0; tf < 4; ++tf) {
       // this pass's operands to registers first, under one LDS wait: the row scale of this
       // lane's token and the bias (and channel scale) of its 16 channel quads
       const float sa = lds_sa[e][wm * 128 + tf * 32 + fr];
-      float4 bq[4][4], cq[4][4];
 #pragma unroll
-      for (int cf = 0; cf < 4; ++cf)
+      for (int cf = 0; cf < 4; ++cf) {
+        float4 bq[1][4], cq[1][4];
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           const int cl = cf * 32 + rq * 8 + g * 4;
-          bq[cf][rq] = *reinterpret_cast<const float4*>(&lds_bias[e][wn * 128 + cl]);
-          if (kChanScale) cq[cf][rq] = *reinterpret_cast<const float4*>(&lds_cs[e][wn * 128 + cl]);
+          bq[0][rq] = *reinterpret_cast<const float4*>(&lds_bias[e][wn * 128 + cl]);
+          if (kChanScale) cq[0][rq] = *reinterpret_cast<const float4*>(&lds_cs[e][wn * 128 + cl]);
         }
-#pragma unroll
-      for (int cf = 0; cf < 4; ++cf) {
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           const int cl = cf * 32 + rq * 8 + g * 4;        // 4 consecutive channels (local)
-          const float bs[4] = {bq[cf][rq].x, bq[cf][rq].y, bq[cf][rq].z, bq[cf][rq].w};
+          const float bs[4] = {bq[0][rq].x, bq[0][rq].y, bq[0][rq].z, bq[0][rq].w};
           float cs[4] = {1.f, 1.f, 1.f, 1.f};
           if (kChanScale) {
-            cs[0] = cq[cf][rq].x; cs[1] = cq[cf][rq].y; cs[2] = cq[cf][rq].z; cs[3] = cq[cf][rq].w;
+            cs[0] = cq[0][rq].x; cs[1] = cq[0][rq].y; cs[2] = cq[0][rq].z; cs[3] = cq[0][rq].w;
           }
           // 0/1 masks of the Q and K segments (multiplies rather than branches keep the
           // epilogue straight-line code); segment boundaries are multiples of 16 channels, so
           // the 8-channel group cf * 32 + rq * 8 lies in one segment and the masks are
           // wave-uniform
-          const int64_t ng8 = n0 + wn * 128 + cf * 32 + rq * 8;
-          const float mq = ng8 < a.Iq ? 1.f : 0.f;
-          const float mk = ng8 >= a.Iq && ng8 < a.Iq + a.Ik ? 1.f : 0.f;
+          const int gi = cf * 4 + rq;
+          const float mq = gi < gq ? 1.f : 0.f;
+          const float mk = gi >= gq && gi < gqk ? 1.f : 0.f;
           float x[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i)
