@@ -183,7 +183,6 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   // takes tiles from the other XCDs' ranges.  Thread 0 claims; the tile id reaches the block
   // through LDS.
   __shared__ int lds_tile[2];
-  __shared__ unsigned lds_ticket;
   const int ntiles = a.tiles_m * a.tiles_n;
   const int per = ntiles / kXcds, rem = ntiles % kXcds;
   const int my_xcd = __builtin_amdgcn_s_getreg(kHwRegXccId) & (kXcds - 1);
@@ -493,28 +492,23 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   };
 
   // ---- tile loop ----
-  // Before the first tile: its stages 0-2 and epilogue operands requested, and a ticket for
-  // the following tile drawn.  Each tile then: waits for everything in flight (stages 0-2 and
-  // operands of this tile, the previous tile's output stores, the ticket), turns the ticket
-  // into the next tile's id (thread 0, into LDS slot e ^ 1), barrier (stage buffer 3, the
-  // previous epilogue's staging area, is free; stages 0-2, the operands and the next tile's id
-  // are visible), requests stage 3, widens the bias, reads stage 0's fragments, barrier, runs
-  // the K-steps.  After the last K-step it requests stages 0-2 and the epilogue operands of
-  // the next tile, which arrive while this tile's epilogue runs, and it draws the ticket after
-  // its output stores (waiting for the atomic there overlaps the stores' drain).
+  // Before the first tile: its stages 0-2 and epilogue operands requested.  Each tile then:
+  // waits for everything in flight (stages 0-2 and operands of this tile, the previous tile's
+  // output stores), barrier (stage buffer 3, the previous epilogue's staging area, is free;
+  // stages 0-2 and the operands are visible), requests stage 3, widens the bias, reads stage
+  // 0's fragments, barrier, runs the K-steps.  Once the last DMA has landed (two K-steps before
+  // the end) thread 0 draws a ticket for the next tile; after the last K-step it turns the
+  // ticket into a tile id, published through LDS, and the block requests that tile's stages
+  // 0-2 and epilogue operands, which arrive while this tile's epilogue runs.
   issue(I0{}, 0);
   issue(I1{}, 1);
   issue(I2{}, 2);
   issue_ops(t, 0);
-  // thread 0 only: a ticket of this XCD's counter, kept in LDS (no register carries it round
-  // the loop)
-  if (tid == 0) lds_ticket = atomicAdd(&a.ctr[my_xcd], 1u);
   // the tile body, instantiated for operand buffer e = 0 and e = 1 (tiles alternate), so the
   // buffer index is a constant everywhere; returns whether another tile follows
   auto tile_iter = [&](auto e_c) __attribute__((always_inline)) -> bool {
     constexpr int e = decltype(e_c)::value;
     wait_vm<0>();
-    if (tid == 0) lds_tile[e ^ 1] = claim((int)lds_ticket);
     __syncthreads();
     issue(I3{}, 3);
     {
@@ -548,6 +542,10 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
       step(I0{}, 0, No{}, W20{}, Z{});             // one superstep only
     }
     step(I1{}, KS - 3, No{}, W0{}, NZ{});
+    // every DMA has landed: draw the ticket for the next tile now (its latency passes during
+    // the last two K-steps); the claim is published after them
+    unsigned ticket;
+    if (tid == 0) ticket = atomicAdd(&a.ctr[my_xcd], 1u);
     step(I2{}, KS - 2, No{}, WN{}, NZ{});
     step(I3{}, KS - 1, No{}, WN{}, NZ{});
     // pin the accumulators here: without this the compiler sinks the last superstep's MFMAs
@@ -559,7 +557,9 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     __builtin_amdgcn_sched_barrier(0);
 
     const Tile cur = t;
-    const int next_tile = __builtin_amdgcn_readfirstlane(lds_tile[e ^ 1]);
+    if (tid == 0) lds_tile[e] = claim((int)ticket);
+    __syncthreads();
+    const int next_tile = __builtin_amdgcn_readfirstlane(lds_tile[e]);
     const bool more = next_tile >= 0;
     if (more) {
       t = decode_tile(next_tile, a.tiles_m, a.tiles_n);
@@ -572,7 +572,6 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     __builtin_amdgcn_sched_barrier(0);
     epilogue(cur, e);
     if (!more) return false;
-    if (tid == 0) lds_ticket = atomicAdd(&a.ctr[my_xcd], 1u);
     return true;
   };
   for (;;) {
