@@ -127,6 +127,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=5, choices=[2, 3, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layout", choices=["bsd", "nbsd"], default="bsd",
+                    help="output layout of the projection and pass 2 (BSD [T, I] or NBSd [I/d, T, d])")
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
@@ -202,7 +204,9 @@ def run_gpu(args):
 
     packed = torch.empty((T, H + 4), dtype=torch.uint8, device=dev)
     res_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if inp["producer"] else None
-    out = torch.empty((T, I), dtype=torch.bfloat16, device=dev)
+    layout = q.LAYOUT_NBSD if args.layout == "nbsd" else q.LAYOUT_BSD
+    out = (torch.empty((I // p.head_dim, T, p.head_dim), dtype=torch.bfloat16, device=dev)
+           if args.layout == "nbsd" else torch.empty((T, I), dtype=torch.bfloat16, device=dev))
     ssq = torch.empty((T, 2), dtype=torch.float32, device=dev)
     ws = torch.empty(q.qkvmx_workspace_bytes(T, H, I), dtype=torch.uint8, device=dev)
     flags = q.NORM_Q | q.NORM_K | q.FUSED_ROPE
@@ -219,12 +223,13 @@ def run_gpu(args):
             ev[1].record(stream)
         q.qkv_rowmx_project(packed, wp, out, H=H, num_heads=p.num_heads,
                             num_kv_heads=p.num_kv_heads, head_dim=p.head_dim, bias=inp["bias"],
-                            ssq=ssq, workspace=ws)
+                            ssq=ssq, workspace=ws, layout=layout)
         if ev:
             ev[2].record(stream)
         q.qk_norm_rope_apply(out, num_heads=p.num_heads, num_kv_heads=p.num_kv_heads,
                              head_dim=p.head_dim, eps=1e-6, flags=flags, ssq=ssq,
-                             q_gamma=inp["gq"], k_gamma=inp["gk"], cos=inp["cos"], sin=inp["sin"])
+                             q_gamma=inp["gq"], k_gamma=inp["gk"], cos=inp["cos"], sin=inp["sin"],
+                             layout=layout)
         if ev:
             ev[3].record(stream)
 
@@ -340,7 +345,8 @@ def main():
                          if r["producer"] else "QKV projection + across-heads norm + RoPE"),
             "T": p.T, "H": p.H, "I": p.I, "num_heads": p.num_heads,
             "num_kv_heads": p.num_kv_heads, "head_dim": p.head_dim,
-            "grid": list(p.grid) if p.grid else None, "parallelism": "single GPU",
+            "grid": list(p.grid) if p.grid else None, "layout": args.layout.upper().replace("NBSD", "NBSd"),
+            "parallelism": "single GPU",
         },
         "roofline": {
             "kernel": "qkv_rowmx_project (activation repack + project_kernel + ssq_reduce)",
@@ -349,7 +355,7 @@ def main():
             "peak": PEAK_MXFP8_TFLOPS,
             "unit": "TFLOP/s",
             "frac": ach / PEAK_MXFP8_TFLOPS,
-            "traffic": measured_traffic() if args.config == 5 else None,
+            "traffic": measured_traffic() if args.config == 5 and args.layout == "bsd" else None,
         },
         "stages": {
             "ms": r["stage_ms"],

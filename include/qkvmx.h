@@ -50,9 +50,13 @@ enum {
   QKVMX_FUSED_ROPE = 4    /* rotate-half RoPE on Q and K after the norm                      */
 };
 
-/* Output layouts ([QKV-CTE] "Interface": output_layout). */
+/* Output layouts ([QKV-CTE] "Interface": output_layout, BSD [B, S, I] or NBSd
+ * [num_heads, B, S, d_head]; B = 1 here, T = S).  With I / d heads in column order (the
+ * num_heads Q heads, then the num_kv_heads K heads, then the V heads), BSD column h * d + j of
+ * token t and NBSd element (h, t, j) hold the same value. */
 enum {
-  QKVMX_LAYOUT_BSD = 0    /* [T, I] row-major, I = (num_heads + 2 * num_kv_heads) * head_dim  */
+  QKVMX_LAYOUT_BSD = 0,   /* [T, I] row-major, I = (num_heads + 2 * num_kv_heads) * head_dim  */
+  QKVMX_LAYOUT_NBSD = 1   /* [I / head_dim, T, head_dim]: (h, t, j) at (h * T + t) * d + j    */
 };
 
 /* Element types of the plain row quantiser's input. */
@@ -136,7 +140,9 @@ size_t qkvmx_workspace_bytes(int64_t T, int64_t H, int64_t I);
  *   w_packed      output of qkv_weight_prepack for this (H, I).
  *   w_channel_scale  fp32 [I] per-output-channel scale ("weight_scales [1, I]"), NULL = 1.
  *   bias          bf16 [I] or NULL.
- *   layout        QKVMX_LAYOUT_BSD: out is [T, I] row-major bf16.
+ *   layout        QKVMX_LAYOUT_BSD: out is [T, I] row-major bf16; QKVMX_LAYOUT_NBSD: out is
+ *                 [I / head_dim, T, head_dim] bf16 (needs 2 ((256 + d) T + 257 d) < 2^31).
+ *                 Any other value is QKVMX_ERR_ARG.
  *   workspace     >= qkvmx_workspace_bytes(T, H, I) bytes, 256-byte aligned, required; its
  *                 contents are scratch (overwritten by every call; calls sharing one workspace
  *                 must be ordered on one stream).
@@ -161,7 +167,8 @@ qkvmx_status qkv_rowmx_project(const uint8_t* a_codes, int64_t a_row_stride,
  *   RoPE: out_j = y_j * cos[t, j'] - y_{j+d/2} * sin[t, j']   for j' = j mod d < d/2,
  *         out_j = y_j * cos[t, j'] + y_{j-d/2} * sin[t, j']   for j' >= d/2  (within each head)
  * and out_j = y_j without QKVMX_FUSED_ROPE.  The result is stored as bf16 in place.
- *   qkv       bf16 [T, I] as written by pass 1 (BSD), I = (num_heads + 2 * num_kv_heads) * d.
+ *   qkv       bf16 output of pass 1 in `layout` (BSD [T, I] or NBSd [I / d, T, d]),
+ *             I = (num_heads + 2 * num_kv_heads) * d; heads are addressed per that layout.
  *   ssq       fp32 [T, 2] (pass 1's sums); required iff a NORM flag is set.
  *   q_gamma   bf16 [num_heads * d], segment-wide; required iff QKVMX_NORM_Q.
  *   k_gamma   bf16 [num_kv_heads * d]; required iff QKVMX_NORM_K, must be NULL otherwise.

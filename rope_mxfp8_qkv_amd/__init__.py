@@ -13,11 +13,11 @@ import os
 from typing import Optional
 
 from . import _abi
-from ._abi import (NORM_Q, NORM_K, FUSED_ROPE, LAYOUT_BSD, DTYPE_F32, DTYPE_BF16, QkvmxError,
+from ._abi import (NORM_Q, NORM_K, FUSED_ROPE, LAYOUT_BSD, LAYOUT_NBSD, DTYPE_F32, DTYPE_BF16, QkvmxError,
                    lib, lib_path)
 
 __all__ = [
-    "NORM_Q", "NORM_K", "FUSED_ROPE", "LAYOUT_BSD", "DTYPE_F32", "DTYPE_BF16", "QkvmxError",
+    "NORM_Q", "NORM_K", "FUSED_ROPE", "LAYOUT_BSD", "LAYOUT_NBSD", "DTYPE_F32", "DTYPE_BF16", "QkvmxError",
     "lib", "lib_path", "mx_weight_quantize", "qkv_weight_packed_bytes", "qkv_weight_prepack",
     "row_quantize_packed", "rmsnorm_mx_quantize", "qkvmx_workspace_bytes", "qkv_rowmx_project",
     "qk_norm_rope_apply", "prepare_weight",
@@ -101,7 +101,8 @@ def qkv_rowmx_project(packed_a, w_packed, out, *, H: int, num_heads: int, num_kv
                       a_scale_stride: Optional[int] = None, layout: int = LAYOUT_BSD,
                       stream=None):
     """Pass 1 on packed ROW_MX rows ``packed_a`` [T, H + 4] (or codes [T, stride] with a
-    separate ``a_scales`` tensor).  ``out`` is bf16 [T, I]; ``ssq`` fp32 [T, 2] or None."""
+    separate ``a_scales`` tensor).  ``out`` is bf16 [T, I] (LAYOUT_BSD) or [I / head_dim, T,
+    head_dim] (LAYOUT_NBSD); ``ssq`` fp32 [T, 2] or None."""
     T = packed_a.shape[0]
     a_ptr = _ptr(packed_a)
     if a_scales is None:
@@ -123,8 +124,9 @@ def qkv_rowmx_project(packed_a, w_packed, out, *, H: int, num_heads: int, num_kv
 def qk_norm_rope_apply(qkv, *, num_heads: int, num_kv_heads: int, head_dim: int, eps: float,
                        flags: int, ssq=None, q_gamma=None, k_gamma=None, cos=None, sin=None,
                        layout: int = LAYOUT_BSD, stream=None):
-    """Pass 2, in place on ``qkv`` (bf16 [T, I])."""
-    T = qkv.shape[0]
+    """Pass 2, in place on ``qkv`` (bf16 [T, I], or [I / head_dim, T, head_dim] with
+    LAYOUT_NBSD)."""
+    T = qkv.shape[1] if layout == LAYOUT_NBSD else qkv.shape[0]
     _check(lib().qk_norm_rope_apply(_ptr(qkv), _ptr(ssq), _ptr(q_gamma), _ptr(k_gamma), _ptr(cos),
                                     _ptr(sin), T, num_heads, num_kv_heads, head_dim, float(eps),
                                     flags, layout, _stream(stream)), "qk_norm_rope_apply")

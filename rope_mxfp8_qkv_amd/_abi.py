@@ -9,6 +9,7 @@ NORM_Q = 1
 NORM_K = 2
 FUSED_ROPE = 4
 LAYOUT_BSD = 0
+LAYOUT_NBSD = 1
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 

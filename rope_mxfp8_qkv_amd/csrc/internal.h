@@ -78,10 +78,11 @@ hipError_t launch_rmsnorm_quantize(const uint16_t* hid, const uint16_t* res, con
 hipError_t launch_project(const uint8_t* a_codes, int64_t a_stride, const uint8_t* a_scales,
                           int64_t s_stride, const uint8_t* w_packed, const float* chan_scale,
                           const uint16_t* bias, int64_t T, int64_t H, int64_t I, int64_t Iq,
-                          int64_t Ik, uint16_t* out, float* ssq, uint8_t* ws, hipStream_t s);
+                          int64_t Ik, int64_t d, bool nbsd, uint16_t* out, float* ssq,
+                          uint8_t* ws, hipStream_t s);
 hipError_t launch_norm_rope(uint16_t* qkv, const float* ssq, const uint16_t* q_gamma,
                             const uint16_t* k_gamma, const float* cos_tab, const float* sin_tab,
                             int64_t T, int nq, int nkv, int d, float eps, uint32_t flags,
-                            hipStream_t s);
+                            bool nbsd, hipStream_t s);
 
 }  // namespace qkvmx

@@ -1,15 +1,15 @@
 // Pass 2 ([QKV-CTE] "Design 1)" steps b-c, "Design 2)", "Design 5)"): across-heads RMSNorm and
-// rotate-half RoPE applied in place to the Q and K columns of the bf16 [T, I] projection; V is
-// never read or written.  HBM-bound: per token 4 * (Iq + Ik) bytes of Q/K plus the token's
-// cos/sin rows (8 * d bytes) and its two sums; gamma is shared by all tokens and stays cached.
+// rotate-half RoPE applied in place to the Q and K heads of the bf16 projection output, in the
+// BSD [T, I] or the NBSd [I / d, T, d] layout; V is never read or written.  HBM-bound: per token
+// 4 * (Iq + Ik) bytes of Q/K plus the token's cos/sin rows (8 * d bytes) and its two sums; gamma
+// is shared by all tokens and stays cached.
 //
-// Thread layout: 64 threads per token; thread (j, hg) owns the 8-lane chunk j0 = 8 j of every
-// head h = hg, hg + G, hg + 2 G, ... (G = 64 / (d / 16) head groups) together with the chunk's
+// Every thread owns an 8-lane chunk j0 of its token's heads together with the chunk's
 // rotate-half partners j0 + d/2 .. j0 + d/2 + 7.  The token's cos/sin values for those 16 lanes
 // and its inv_rms are loaded once per thread and reused for every head, as the pages broadcast
 // the position-only tables across heads; each head costs two independent 16-byte loads of x
-// (plus gamma, an L1/L2 hit) and two 16-byte streaming stores.  The 8 threads of a head read
-// 2 x 128 contiguous bytes (d = 128).  inv_rms is folded into the gamma multiply.
+// (plus gamma, an L1/L2 hit) and two 16-byte streaming stores.  inv_rms is folded into the gamma
+// multiply.  The two layouts differ only in how threads map to (token, head): see the kernels.
 #include "device_common.h"
 #include "internal.h"
 
@@ -59,18 +59,14 @@ __device__ __forceinline__ void load8f(const float* p, float (&f)[8]) {
   f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
-__global__ void __launch_bounds__(kThreadsPerToken * kTokensPerBlock) norm_rope_kernel(
-    const NormRopeArgs a) {
-  const int64_t token = (int64_t)blockIdx.x * kTokensPerBlock + (threadIdx.x / kThreadsPerToken);
-  if (token >= a.T) return;
-  const int lane = threadIdx.x % kThreadsPerToken;
-  const int cpd = a.d / 16;                 // chunks per head half-pair
-  const int ngroups = kThreadsPerToken / cpd;
-  const int j0 = (lane % cpd) * 8;
-  const int hg = lane / cpd;
+// One token's work for one thread: the 8-lane chunk j0 (and its rotate-half partners
+// j0 + d/2 ..) of the touched heads h = h0, h0 + hstep, ...; base_of(h, is_k) addresses the
+// head's d elements for this token.  The token's cos/sin values and inv_rms are loaded once and
+// reused for every head.
+template <typename BaseOf>
+__device__ __forceinline__ void apply_token(const NormRopeArgs& a, int64_t token, int j0, int h0,
+                                            int hstep, BaseOf base_of) {
   const int half = a.d / 2;
-  if (hg >= ngroups) return;                // lanes past the last whole group (64 % cpd != 0)
-
   float clo[8], chi[8], slo[8], shi[8];
   if (a.rope) {
     const float* cr = a.cos_tab + token * a.d;
@@ -83,15 +79,10 @@ __global__ void __launch_bounds__(kThreadsPerToken * kTokensPerBlock) norm_rope_
   float rq = 1.0f, rk = 1.0f;
   if (a.norm_q) rq = 1.0f / sqrtf(a.ssq[token * 2] / (float)(a.nq * a.d) + a.eps);
   if (a.norm_k) rk = 1.0f / sqrtf(a.ssq[token * 2 + 1] / (float)(a.nkv * a.d) + a.eps);
-
-  uint16_t* row = a.qkv + token * a.I;
 #pragma unroll 4
-  for (int h = hg; h < a.heads; h += ngroups) {
+  for (int h = h0; h < a.heads; h += hstep) {
     const bool is_k = h >= a.heads_q;
-    // column of the head: Q heads come first; the K segment starts at nq * d
-    const int64_t col = is_k ? (int64_t)a.nq * a.d + (int64_t)(h - a.heads_q) * a.d
-                             : (int64_t)h * a.d;
-    uint16_t* base = row + col;
+    uint16_t* base = base_of(h, is_k);
     float lo[8], hi[8];
     unpack8(*reinterpret_cast<const uint4*>(base + j0), lo);
     unpack8(*reinterpret_cast<const uint4*>(base + half + j0), hi);
@@ -122,12 +113,50 @@ __global__ void __launch_bounds__(kThreadsPerToken * kTokensPerBlock) norm_rope_
   }
 }
 
+// BSD [T, I]: 64 threads per token; thread (j, hg) owns chunk j0 = 8 j of heads hg, hg + G, ...
+// (G = 64 / (d / 16) head groups), so one wave instruction covers G heads of one token row.
+__global__ void __launch_bounds__(kThreadsPerToken * kTokensPerBlock) norm_rope_kernel(
+    const NormRopeArgs a) {
+  const int64_t token = (int64_t)blockIdx.x * kTokensPerBlock + (threadIdx.x / kThreadsPerToken);
+  if (token >= a.T) return;
+  const int lane = threadIdx.x % kThreadsPerToken;
+  const int cpd = a.d / 16;                 // chunks per head half-pair
+  const int ngroups = kThreadsPerToken / cpd;
+  const int hg = lane / cpd;
+  if (hg >= ngroups) return;                // lanes past the last whole group (64 % cpd != 0)
+  uint16_t* row = a.qkv + token * a.I;
+  apply_token(a, token, (lane % cpd) * 8, hg, ngroups, [&](int h, bool is_k) {
+    // Q heads come first; the K segment starts at nq * d
+    return row + (is_k ? (int64_t)a.nq * a.d + (int64_t)(h - a.heads_q) * a.d : (int64_t)h * a.d);
+  });
+}
+
+// NBSd [I / d, T, d] ([QKV-CTE] "Interface": output_layout; "Design 2)": each head occupies its
+// own block of rows, d contiguous): lane -> (token, chunk) with the chunk fastest, so for each
+// head one wave instruction covers 64 / (d / 16) consecutive tokens of that head, contiguous in
+// memory; every thread walks all touched heads of its token.
+__global__ void __launch_bounds__(kThreadsPerToken * kTokensPerBlock) norm_rope_nbsd_kernel(
+    const NormRopeArgs a) {
+  const int cpd = a.d / 16;
+  const int tpw = kThreadsPerToken / cpd;   // tokens per wavefront
+  const int lane = threadIdx.x % kThreadsPerToken, wave = threadIdx.x / kThreadsPerToken;
+  const int slot = lane / cpd;
+  if (slot >= tpw) return;                  // lanes past the last whole token (64 % cpd != 0)
+  const int64_t token = ((int64_t)blockIdx.x * kTokensPerBlock + wave) * tpw + slot;
+  if (token >= a.T) return;
+  apply_token(a, token, (lane % cpd) * 8, 0, 1, [&](int h, bool is_k) {
+    // head index in the output: Q heads first, then K heads (which follow all nq Q heads)
+    const int64_t hid = is_k ? (int64_t)a.nq + (h - a.heads_q) : (int64_t)h;
+    return a.qkv + (hid * a.T + token) * a.d;
+  });
+}
+
 }  // namespace
 
 hipError_t launch_norm_rope(uint16_t* qkv, const float* ssq, const uint16_t* q_gamma,
                             const uint16_t* k_gamma, const float* cos_tab, const float* sin_tab,
                             int64_t T, int nq, int nkv, int d, float eps, uint32_t flags,
-                            hipStream_t s) {
+                            bool nbsd, hipStream_t s) {
   NormRopeArgs a;
   a.qkv = qkv; a.ssq = ssq; a.gq = q_gamma; a.gk = k_gamma; a.cos_tab = cos_tab;
   a.sin_tab = sin_tab; a.T = T; a.I = (int64_t)(nq + 2 * nkv) * d;
@@ -139,9 +168,14 @@ hipError_t launch_norm_rope(uint16_t* qkv, const float* ssq, const uint16_t* q_g
   a.heads = a.heads_q + (k_on ? nkv : 0);
   if (a.heads == 0 || T == 0) return hipSuccess;        // nothing to do
   if (d / 16 > kThreadsPerToken) return hipErrorInvalidValue;
-  const int64_t blocks = ceil_div(T, kTokensPerBlock);
-  hipLaunchKernelGGL(norm_rope_kernel, dim3((unsigned)blocks),
-                     dim3(kThreadsPerToken * kTokensPerBlock), 0, s, a);
+  if (nbsd) {
+    const int64_t per_block = (int64_t)kTokensPerBlock * (kThreadsPerToken / (d / 16));
+    hipLaunchKernelGGL(norm_rope_nbsd_kernel, dim3((unsigned)ceil_div(T, per_block)),
+                       dim3(kThreadsPerToken * kTokensPerBlock), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(norm_rope_kernel, dim3((unsigned)ceil_div(T, kTokensPerBlock)),
+                       dim3(kThreadsPerToken * kTokensPerBlock), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -59,6 +59,7 @@ constexpr int kHwRegXccId = 20 | (31 << 11);        // s_getreg operand: XCC_ID,
 constexpr int kBufs = 4;                           // LDS stage buffers
 constexpr int kBufferRsrcWord3 = 0x00020000;        // buffer descriptor word 3 (gfx9 family)
 constexpr int kNonTemporal = 2;                    // buffer store cache policy: streaming
+constexpr uint32_t kDropOffset = 0x80000000u;      // outside any descriptor range (<= 2^31 - 1)
 constexpr int kDmaPerStage = 8;                    // per wave: 4 (weight) + 4 (activation)
                                                    // (+ 2 exponent DMAs every 4th stage)
 
@@ -73,6 +74,7 @@ struct ProjectArgs {
   const float* chan_scale;     // [I] or null
   const uint16_t* bias;        // [I] or null
   int64_t T, H, I, Iq, Ik;
+  int64_t d;                   // head_dim (NBSd addressing)
   int KS;                      // K-stages of 64 bytes (multiple of 4)
   int tiles_m, tiles_n;
   uint16_t* out;
@@ -156,7 +158,7 @@ __device__ __forceinline__ Tile decode_tile(int tile, int tiles_m, int tiles_n) 
   return Tile{first_m + in_group % gm, in_group / gm};
 }
 
-template <bool kChanScale, bool kBias>
+template <bool kChanScale, bool kBias, bool kNbsd>
 __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_w[kBufs][kStageImage];
   __shared__ __attribute__((aligned(16))) uint8_t lds_x[kBufs][kStageImage];
@@ -400,16 +402,40 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     const int jc = el & 15;
     const int64_t ch = n0 + wn * 128 + jc * 8;
     const bool ch_ok = ch < a.I;
-    // the tile's output through a buffer descriptor whose range ends where the output array
-    // ends: stores to token rows >= T fall outside it and are dropped by the hardware's range
-    // check, so row bounds need no per-store predicate (in-tile offsets are < 256 * I * 2,
-    // which the host keeps below 2^31)
-    const int64_t out_left = ((a.T - m0) * a.I - n0) * 2;
-    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-        a.out + m0 * a.I + n0, (short)0, (int)(uint32_t)min(out_left, (int64_t)0x7FFFFFFF),
-        kBufferRsrcWord3);
-    const uint32_t row_bytes = (uint32_t)a.I * 2;
-    const uint32_t lane_off = (uint32_t)(wm * 128 + (el >> 4)) * row_bytes + (uint32_t)(wn * 128 + jc * 8) * 2;
+    // The tile's output through a buffer descriptor (raw, stride 0); the per-store step is one
+    // token row.  BSD [T, I]: the descriptor's range ends where the output array ends, so
+    // stores to token rows >= T fall outside it and the hardware's range check drops them (no
+    // per-store predicate); in-tile offsets are < 256 * I * 2, which the host keeps below 2^31.
+    // NBSd [I / d, T, d]: a row >= T of one head would alias the next head's first rows, so
+    // invalid stores get an offset of 2^31, beyond every range the descriptor can hold.
+    __amdgpu_buffer_rsrc_t orsrc;
+    uint32_t row_bytes, lane_off;
+    int rows_left = 0;             // NBSd: this lane's valid token rows (0 for channels >= I)
+    if (!kNbsd) {
+      const int64_t out_left = ((a.T - m0) * a.I - n0) * 2;
+      orsrc = __builtin_amdgcn_make_buffer_rsrc(
+          a.out + m0 * a.I + n0, (short)0, (int)(uint32_t)min(out_left, (int64_t)0x7FFFFFFF),
+          kBufferRsrcWord3);
+      row_bytes = (uint32_t)a.I * 2;
+      lane_off = (uint32_t)(wm * 128 + (el >> 4)) * row_bytes + (uint32_t)(wn * 128 + jc * 8) * 2;
+    } else {
+      // element (token t, channel c) at ((c / d) * T + t) * d + c % d; base = the tile's first
+      // head hb at token m0
+      // channels < I < 2^22 and d < 2^11: 32-bit unsigned division (a 64-bit one expands into
+      // a long branchy sequence)
+      const uint32_t dd = (uint32_t)a.d;
+      const int64_t hb = (uint32_t)n0 / dd;
+      const int64_t base_el = hb * a.T * a.d + m0 * a.d;
+      const int64_t hh = (uint32_t)ch / dd, jj = ch - hh * a.d;
+      const int64_t out_left = (a.T * a.I - base_el) * 2;
+      orsrc = __builtin_amdgcn_make_buffer_rsrc(
+          a.out + base_el, (short)0, (int)(uint32_t)min(out_left, (int64_t)0x7FFFFFFF),
+          kBufferRsrcWord3);
+      row_bytes = (uint32_t)a.d * 2;
+      lane_off = (uint32_t)((((hh - hb) * a.T + wm * 128 + (el >> 4)) * a.d + jj) * 2);
+      rows_left = ch_ok ? (int)min(max(a.T - (m0 + wm * 128 + (el >> 4)), (int64_t)0), (int64_t)256)
+                        : 0;
+    }
     float sq_q[4] = {0.f, 0.f, 0.f, 0.f}, sq_k[4] = {0.f, 0.f, 0.f, 0.f};
     // number of this wave's 8-channel groups (of 16) inside Q, and inside Q or K (uniform)
     const int64_t c0 = n0 + wn * 128;
@@ -470,9 +496,15 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
         // bit 4 of the row is bit 2 of j: those rows hold their 8-byte halves swapped
         const u32x4 o = ((j >> 2) & 1) ? u32x4{v[j].z, v[j].w, v[j].x, v[j].y}
                                        : u32x4{v[j].x, v[j].y, v[j].z, v[j].w};
-        if (ch_ok)
-          __builtin_amdgcn_raw_buffer_store_b128(o, orsrc, (int)(obyte + (uint32_t)(j * 4) * row_bytes),
-                                                 0, kNonTemporal);
+        if (!kNbsd) {
+          if (ch_ok)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                o, orsrc, (int)(obyte + (uint32_t)(j * 4) * row_bytes), 0, kNonTemporal);
+        } else {
+          const bool ok = tf * 32 + j * 4 < rows_left;
+          const uint32_t off = ok ? obyte + (uint32_t)(j * 4) * row_bytes : kDropOffset;
+          __builtin_amdgcn_raw_buffer_store_b128(o, orsrc, (int)off, 0, kNonTemporal);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);      // passes stay in order: bounded register use
     }
@@ -625,14 +657,15 @@ __global__ void __launch_bounds__(256) ssq_reduce_kernel(const float* __restrict
 hipError_t launch_project(const uint8_t* a_codes, int64_t a_stride, const uint8_t* a_scales,
                           int64_t s_stride, const uint8_t* w_packed, const float* chan_scale,
                           const uint16_t* bias, int64_t T, int64_t H, int64_t I, int64_t Iq,
-                          int64_t Ik, uint16_t* out, float* ssq, uint8_t* ws, hipStream_t s) {
+                          int64_t Ik, int64_t d, bool nbsd, uint16_t* out, float* ssq,
+                          uint8_t* ws, hipStream_t s) {
   ProjectArgs a;
   a.a_codes = a_codes; a.a_stride = a_stride; a.a_scales = a_scales; a.s_stride = s_stride;
   a.w_img = w_packed;
   a.w_scales = w_packed + packed_scales_offset(H, I);
   a.x_img = ws;
   a.chan_scale = chan_scale; a.bias = bias;
-  a.T = T; a.H = H; a.I = I; a.Iq = Iq; a.Ik = Ik;
+  a.T = T; a.H = H; a.I = I; a.Iq = Iq; a.Ik = Ik; a.d = d;
   a.KS = (int)packed_stages(H);
   a.tiles_m = (int)ceil_div(T, kTileM);
   a.tiles_n = (int)packed_tiles_n(I);
@@ -654,14 +687,17 @@ hipError_t launch_project(const uint8_t* a_codes, int64_t a_stride, const uint8_
   const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n;
   const unsigned nblocks = (unsigned)std::min<int64_t>(ntiles, std::max(cus, 1));
   const dim3 grid(nblocks), block(kThreads);
-  if (chan_scale && bias)
-    hipLaunchKernelGGL((project_kernel<true, true>), grid, block, 0, s, a);
-  else if (chan_scale)
-    hipLaunchKernelGGL((project_kernel<true, false>), grid, block, 0, s, a);
-  else if (bias)
-    hipLaunchKernelGGL((project_kernel<false, true>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((project_kernel<false, false>), grid, block, 0, s, a);
+  const int variant = (chan_scale ? 4 : 0) | (bias ? 2 : 0) | (nbsd ? 1 : 0);
+  switch (variant) {
+    case 0: hipLaunchKernelGGL((project_kernel<false, false, false>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((project_kernel<false, false, true>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((project_kernel<false, true, false>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((project_kernel<false, true, true>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((project_kernel<true, false, false>), grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL((project_kernel<true, false, true>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((project_kernel<true, true, false>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((project_kernel<true, true, true>), grid, block, 0, s, a); break;
+  }
   e = hipGetLastError();
   if (e != hipSuccess || !ssq) return e;
   // only the partials of 128-channel groups that overlap Q or K are written and summed

@@ -126,7 +126,8 @@ qkvmx_status qkv_rowmx_project(const uint8_t* a_codes, int64_t a_row_stride,
   if (T <= 0 || H <= 0 || H % 32) return fail(QKVMX_ERR_SHAPE, "qkv_rowmx_project: need T > 0, H %% 32 == 0");
   if (num_heads < 1 || num_kv_heads < 0 || head_dim <= 0 || head_dim % 16)
     return fail(QKVMX_ERR_SHAPE, "qkv_rowmx_project: need num_heads >= 1, num_kv_heads >= 0, head_dim %% 16 == 0");
-  if (layout != QKVMX_LAYOUT_BSD) return fail(QKVMX_ERR_UNSUPPORTED, "qkv_rowmx_project: only the BSD layout is built");
+  if (layout != QKVMX_LAYOUT_BSD && layout != QKVMX_LAYOUT_NBSD)
+    return fail(QKVMX_ERR_ARG, "qkv_rowmx_project: layout must be QKVMX_LAYOUT_BSD or QKVMX_LAYOUT_NBSD");
   if (a_row_stride < H || a_row_stride % 4 || a_scale_stride <= 0 || a_scale_stride % 4)
     return fail(QKVMX_ERR_SHAPE, "qkv_rowmx_project: a_row_stride >= H and strides multiples of 4");
   const int64_t I = (int64_t)(num_heads + 2 * (int64_t)num_kv_heads) * head_dim;
@@ -134,6 +135,9 @@ qkvmx_status qkv_rowmx_project(const uint8_t* a_codes, int64_t a_row_stride,
     return fail(QKVMX_ERR_UNSUPPORTED, "qkv_rowmx_project: activation span must be < 2^31 bytes");
   if (I * 2 * 256 >= kMaxOffset)     // byte offsets within one 256-token output tile
     return fail(QKVMX_ERR_UNSUPPORTED, "qkv_rowmx_project: I must be < 2^22");
+  // NBSd: byte offsets from a tile's first head to the rows it writes
+  if (layout == QKVMX_LAYOUT_NBSD && 2 * ((256 + (int64_t)head_dim) * T + 257 * (int64_t)head_dim) >= kMaxOffset)
+    return fail(QKVMX_ERR_UNSUPPORTED, "qkv_rowmx_project: NBSd needs 2 ((256 + head_dim) T + 257 head_dim) < 2^31");
   if (ws_bytes < workspace_total_bytes(T, H, I))
     return fail(QKVMX_ERR_WORKSPACE, "qkv_rowmx_project: workspace %zu < %zu bytes", ws_bytes, workspace_total_bytes(T, H, I));
   if (!aligned(a_codes, 4) || !aligned(a_scales, 4) || !aligned(w_packed, 256) ||
@@ -143,7 +147,8 @@ qkvmx_status qkv_rowmx_project(const uint8_t* a_codes, int64_t a_row_stride,
   const int64_t Iq = (int64_t)num_heads * head_dim, Ik = (int64_t)num_kv_heads * head_dim;
   return hip_status(launch_project(a_codes, a_row_stride, a_scales, a_scale_stride,
                                    (const uint8_t*)w_packed, w_channel_scale, bias, T, H, I, Iq,
-                                   Ik, out, ssq, (uint8_t*)workspace, stream), "qkv_rowmx_project");
+                                   Ik, head_dim, layout == QKVMX_LAYOUT_NBSD, out, ssq,
+                                   (uint8_t*)workspace, stream), "qkv_rowmx_project");
 }
 
 qkvmx_status qk_norm_rope_apply(uint16_t* qkv, const float* ssq, const uint16_t* q_gamma,
@@ -156,7 +161,8 @@ qkvmx_status qk_norm_rope_apply(uint16_t* qkv, const float* ssq, const uint16_t*
     return fail(QKVMX_ERR_ARG, "qk_norm_rope_apply: unknown flag bits");
   if (T <= 0 || num_heads < 1 || num_kv_heads < 0 || head_dim <= 0 || head_dim % 16)
     return fail(QKVMX_ERR_SHAPE, "qk_norm_rope_apply: need T > 0, num_heads >= 1, num_kv_heads >= 0, head_dim %% 16 == 0");
-  if (layout != QKVMX_LAYOUT_BSD) return fail(QKVMX_ERR_UNSUPPORTED, "qk_norm_rope_apply: only the BSD layout is built");
+  if (layout != QKVMX_LAYOUT_BSD && layout != QKVMX_LAYOUT_NBSD)
+    return fail(QKVMX_ERR_ARG, "qk_norm_rope_apply: layout must be QKVMX_LAYOUT_BSD or QKVMX_LAYOUT_NBSD");
   if (head_dim > 1024) return fail(QKVMX_ERR_UNSUPPORTED, "qk_norm_rope_apply: head_dim > 1024");
   if ((flags & QKVMX_FUSED_ROPE) && (!cos_tab || !sin_tab))
     return fail(QKVMX_ERR_ARG, "qk_norm_rope_apply: QKVMX_FUSED_ROPE needs cos_tab and sin_tab");
@@ -172,7 +178,8 @@ qkvmx_status qk_norm_rope_apply(uint16_t* qkv, const float* ssq, const uint16_t*
       (sin_tab && !aligned(sin_tab, 16)))
     return fail(QKVMX_ERR_ALIGN, "qk_norm_rope_apply: qkv/gamma/tables 16-byte, ssq 8-byte aligned");
   return hip_status(launch_norm_rope(qkv, ssq, q_gamma, k_gamma, cos_tab, sin_tab, T, num_heads,
-                                     num_kv_heads, head_dim, eps, flags, stream), "qk_norm_rope_apply");
+                                     num_kv_heads, head_dim, eps, flags,
+                                     layout == QKVMX_LAYOUT_NBSD, stream), "qk_norm_rope_apply");
 }
 
 }  // extern "C"

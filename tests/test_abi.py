@@ -57,6 +57,20 @@ def test_size_queries():
 P = 0x10000   # a fake, well-aligned device address: validation fails before it is used
 
 
+@pytest.fixture(autouse=True)
+def _no_gpu_launches():
+    """These checks hand the library fake pointers and rely on validation failing first; where
+    a GPU is present a check that unexpectedly passed validation would launch a kernel on them,
+    so the module runs only on hosts without one."""
+    try:
+        import torch
+        if torch.cuda.device_count() > 0:
+            pytest.skip("fake-pointer validation checks run on GPU-less hosts only")
+    except ImportError:
+        pass
+    yield
+
+
 def _proj(L, **kw):
     a = dict(a_codes=P, a_row_stride=260, a_scales=P + 256, a_scale_stride=260, w_packed=P,
              w_channel_scale=None, bias=None, T=4, H=256, num_heads=2, num_kv_heads=2,
@@ -79,7 +93,8 @@ def test_projection_validation():
     assert _proj(L, H=100, a_row_stride=104, a_scale_stride=104) == 2
     assert _proj(L, head_dim=40) == 2
     assert _proj(L, T=0) == 2
-    assert _proj(L, layout=1) == 6
+    assert _proj(L, layout=2) == 4                                # unknown layout
+    assert _proj(L, layout=1, T=4_000_000) == 6                   # NBSd offsets past 2^31
     assert _proj(L, a_row_stride=258) == 2
     assert _proj(L, workspace=None) == 5                          # workspace is required
     assert _proj(L, ssq=P, workspace=P, ws_bytes=8) == 5          # workspace too small
@@ -102,7 +117,7 @@ def test_norm_rope_validation():
     assert _nr(L, flags=8) == 4
     assert _nr(L, head_dim=24) == 2
     assert _nr(L, eps=-1.0) == 4
-    assert _nr(L, layout=1) == 6
+    assert _nr(L, layout=2) == 4                                  # unknown layout
     assert _nr(L, qkv=P + 8) == 3
 
 
