@@ -22,11 +22,12 @@ from .rowmx import rowmx_quantize, rowmx_unpack
 from .mxweight import mx_weight_quantize, mx_weight_decode
 from .gemm import project, segment_ssq
 from .norm_rope import inv_rms, norm_rope
-from .producer import rmsnorm_rowmx
+from .producer import rmsnorm_rowmx, rmsnorm_mx
+from .mxact import mx_block_quantize, mx_block_decode
 from .layouts import bsd_to_nbsd, nbsd_to_bsd
 
 __all__ = [
     "e4m3_decode", "e4m3_encode", "e8m0_decode", "bf16_round_f32", "bf16_to_f64", "f64_to_bf16",
     "rowmx_quantize", "rowmx_unpack", "mx_weight_quantize", "mx_weight_decode",
-    "project", "segment_ssq", "inv_rms", "norm_rope", "rmsnorm_rowmx", "bsd_to_nbsd", "nbsd_to_bsd",
+    "project", "segment_ssq", "inv_rms", "norm_rope", "rmsnorm_rowmx", "rmsnorm_mx", "mx_block_quantize", "mx_block_decode", "bsd_to_nbsd", "nbsd_to_bsd",
 ]

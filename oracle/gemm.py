@@ -10,7 +10,8 @@ fp32 dequant scale ``[1, I]``; ``bias`` is ``[1, I]``; the result is bf16.
 Dequantisation used (the plain reading of the two scale kinds):
   X[s, i] = sA[s] * c[i] * sum_h dec(A[s, h]) * dec(W[h, i]) * 2^(E[h // 32, i] - 127) + bias[i]
 with sA the row's fp32 ROW_MX scale, c the per-channel weight scale (1 when absent) and E the
-block exponent.  Everything is evaluated in float64; the bf16 output is one rounding of X.
+block exponent.  With MX block-32 activations ([RMSNORM-MX] ``qmx_output_dtype``) the row scale
+is replaced by a per-block factor inside the sum: dec(A[s, h]) * 2^(Ea[s, h // 32] - 127).  Everything is evaluated in float64; the bf16 output is one rounding of X.
 
 [QKV-CTE] "Design 1)", step a: per token, the sum of x^2 over the whole Q segment and over the
 whole K segment of the un-normalised output; V is excluded.  "Design 5)": with
@@ -21,6 +22,7 @@ from __future__ import annotations
 import numpy as np
 
 from .codecs import bf16_to_f64, e4m3_decode
+from .mxact import mx_block_decode
 from .mxweight import mx_weight_decode
 
 
@@ -37,15 +39,23 @@ def segment_ssq(X, num_heads: int, num_kv_heads: int, head_dim: int) -> np.ndarr
 
 
 def project(a_codes, a_scale, w_codes, w_e8m0, w_channel_scale=None, bias_bf16=None, *,
-            num_heads: int, num_kv_heads: int, head_dim: int, w_dense=None):
+            num_heads: int, num_kv_heads: int, head_dim: int, w_dense=None, a_e8m0=None):
     """Returns (X float64 [T, I] before rounding, ssq float64 [T, 2]).
 
     a_codes uint8 [T, H]; a_scale fp32 [T]; w_codes uint8 [H // 4, I, 4]; w_e8m0 uint8
     [H // 32, I]; w_channel_scale fp32 [I] or None; bias_bf16 uint16 [I] or None.
     ``w_dense`` may pass a pre-decoded float64 W [H, I] (same values as decoding the codes)
     so that repeated calls on row samples do not decode the weight again.
+    MX block-32 activations: pass ``a_e8m0`` uint8 [T, H // 32] and ``a_scale=None``; the
+    activation is then dec(A[s, h]) * 2^(Ea[s, h // 32] - 127) and there is no row scale.
     """
-    A = e4m3_decode(a_codes)                                          # [T, H]
+    if a_e8m0 is not None:
+        if a_scale is not None:
+            raise ValueError("MX block-32 activations carry no row scale")
+        A = mx_block_decode(a_codes, a_e8m0)                          # [T, H]
+        a_scale = np.ones(A.shape[0], np.float32)
+    else:
+        A = e4m3_decode(a_codes)                                      # [T, H]
     W = mx_weight_decode(w_codes, w_e8m0) if w_dense is None else w_dense
     T, H = A.shape
     I = W.shape[1]
