@@ -60,6 +60,7 @@ constexpr int kBufs = 4;                           // LDS stage buffers
 constexpr int kBufferRsrcWord3 = 0x00020000;        // buffer descriptor word 3 (gfx9 family)
 constexpr int kNonTemporal = 2;                    // buffer store cache policy: streaming
 constexpr uint32_t kDropOffset = 0x80000000u;      // outside any descriptor range (<= 2^31 - 1)
+constexpr int kTailStores = 8;                   // unconditional stores ending an epilogue
 constexpr int kDmaPerStage = 8;                    // per wave: 4 (weight) + 4 (activation)
                                                    // (+ 2 exponent DMAs every 4th stage)
 
@@ -392,7 +393,12 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   // all eight reads in flight before their stores) and stores 16-byte vectors.  Streaming
   // (non-temporal) stores: the output is not re-read by this kernel, and keeping it out of L2
   // leaves L2 to the operand stage images that neighbouring tiles share.
-  auto epilogue = [&](Tile u, int e) __attribute__((always_inline)) {
+  // With `more`, pass p (p < 3) also requests the next tile's stage p and pass 3 its epilogue
+  // operands, so the address unit works through them while the passes compute instead of
+  // receiving them as one burst.  Pass 3 ends with exactly kTailStores unconditional stores
+  // per wave after its last DMA (vector memory operations complete in issue order), so the
+  // next tile only waits for the DMAs, not for those stores.
+  auto epilogue = [&](Tile u, int e, bool more, Tile nxt) __attribute__((always_inline)) {
     // lane-derived addresses are recomputed here from a fresh lane index, so the compiler
     // cannot hoist them out of the tile loop and keep them live through the K-steps
     const int el = fresh_lane();
@@ -443,6 +449,11 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     const int gqk = __builtin_amdgcn_readfirstlane((int)min(max((a.Iq + a.Ik - c0) / 8, (int64_t)0), (int64_t)16));
 #pragma unroll
     for (int tf = 0; tf < 4; ++tf) {
+      if (more) {
+        if (tf == 0) issue(I0{}, 0);
+        if (tf == 1) issue(I1{}, 1);
+        if (tf == 2) issue(I2{}, 2);
+      }
       // this pass's operands to registers first, under one LDS wait: the row scale of this
       // lane's token and the bias (and channel scale) of its 16 channel quads
       const float sa = lds_sa[e][wm * 128 + tf * 32 + fr];
@@ -484,6 +495,25 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
                                        ((g ^ (fr >> 4)) & 1) * 8) = o;
         }
       }
+      if (tf == 3) {
+        // every pass's sums are complete: the per-token partials go out before the last
+        // DMAs, then the next tile's epilogue operands
+        if (a.ws && n0 + wn * 128 < a.Iq + a.Ik) {      // this wave's channels overlap Q or K
+          const int64_t p = (int64_t)u.tn * 2 + wn;
+#pragma unroll
+          for (int tq = 0; tq < 4; ++tq) {
+            const float q = add_xor32(sq_q[tq]);
+            const float k = add_xor32(sq_k[tq]);
+            const int64_t tok = m0 + wm * 128 + tq * 32 + fr;
+            if (g == 0 && tok < a.T) {
+              u32x2_a8 o = {__float_as_uint(q), __float_as_uint(k)};
+              *reinterpret_cast<u32x2_a8*>(a.ws + (p * a.T + tok) * 2) = o;
+            }
+          }
+        }
+        if (more) issue_ops(nxt, e ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const uint32_t obyte = lane_off + (uint32_t)(tf * 32) * row_bytes;
       uint4 v[8];
 #pragma unroll
@@ -497,50 +527,42 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
         const u32x4 o = ((j >> 2) & 1) ? u32x4{v[j].z, v[j].w, v[j].x, v[j].y}
                                        : u32x4{v[j].x, v[j].y, v[j].z, v[j].w};
         if (!kNbsd) {
-          if (ch_ok)
-            __builtin_amdgcn_raw_buffer_store_b128(
-                o, orsrc, (int)(obyte + (uint32_t)(j * 4) * row_bytes), 0, kNonTemporal);
+          const uint32_t off = ch_ok ? obyte + (uint32_t)(j * 4) * row_bytes : kDropOffset;
+          __builtin_amdgcn_raw_buffer_store_b128(o, orsrc, (int)off, 0, kNonTemporal);
         } else {
           const bool ok = tf * 32 + j * 4 < rows_left;
           const uint32_t off = ok ? obyte + (uint32_t)(j * 4) * row_bytes : kDropOffset;
           __builtin_amdgcn_raw_buffer_store_b128(o, orsrc, (int)off, 0, kNonTemporal);
         }
       }
+      // the pass's sums are formed here, from registers (otherwise the compiler sinks every
+      // pass's sum-of-squares arithmetic below the last pass, parking the fp32 values in
+      // AGPRs meanwhile)
+      asm volatile("" :: "v"(sq_q[tf]), "v"(sq_k[tf]));
       __builtin_amdgcn_sched_barrier(0);      // passes stay in order: bounded register use
-    }
-    if (a.ws && n0 + wn * 128 < a.Iq + a.Ik) {      // this wave's channels overlap Q or K
-      const int64_t p = (int64_t)u.tn * 2 + wn;
-#pragma unroll
-      for (int tf = 0; tf < 4; ++tf) {
-        const float q = add_xor32(sq_q[tf]);
-        const float k = add_xor32(sq_k[tf]);
-        const int64_t tok = m0 + wm * 128 + tf * 32 + fr;
-        if (g == 0 && tok < a.T) {
-          u32x2_a8 o = {__float_as_uint(q), __float_as_uint(k)};
-          *reinterpret_cast<u32x2_a8*>(a.ws + (p * a.T + tok) * 2) = o;
-        }
-      }
     }
   };
 
   // ---- tile loop ----
-  // Before the first tile: its stages 0-2 and epilogue operands requested.  Each tile then:
-  // waits for everything in flight (stages 0-2 and operands of this tile, the previous tile's
-  // output stores), barrier (stage buffer 3, the previous epilogue's staging area, is free;
-  // stages 0-2 and the operands are visible), requests stage 3, widens the bias, reads stage
-  // 0's fragments, barrier, runs the K-steps.  Once the last DMA has landed (two K-steps before
-  // the end) thread 0 draws a ticket for the next tile; after the last K-step it turns the
-  // ticket into a tile id, published through LDS, and the block requests that tile's stages
-  // 0-2 and epilogue operands, which arrive while this tile's epilogue runs.
+  // Before the first tile: its stages 0-2 and epilogue operands requested and awaited.  Each
+  // tile then: waits for everything in flight except the previous epilogue's last
+  // kTailStores stores, barrier (stage buffer 3, the previous epilogue's staging area, is
+  // free; stages 0-2 and the operands are visible), requests stage 3, widens the bias, reads
+  // stage 0's fragments, barrier, runs the K-steps.  Once the last DMA has landed (two K-steps
+  // before the end) thread 0 draws a ticket for the next tile; after the last K-step it turns
+  // the ticket into a tile id, published through LDS, and the epilogue's passes request that
+  // tile's stages 0-2 and epilogue operands one after another.
   issue(I0{}, 0);
   issue(I1{}, 1);
   issue(I2{}, 2);
   issue_ops(t, 0);
+  wait_vm<0>();
   // the tile body, instantiated for operand buffer e = 0 and e = 1 (tiles alternate), so the
   // buffer index is a constant everywhere; returns whether another tile follows
   auto tile_iter = [&](auto e_c) __attribute__((always_inline)) -> bool {
     constexpr int e = decltype(e_c)::value;
-    wait_vm<0>();
+    // the previous epilogue's DMAs have landed; its last kTailStores stores may be in flight
+    wait_vm<kTailStores>();
     __syncthreads();
     issue(I3{}, 3);
     {
@@ -596,15 +618,10 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     if (more) {
       t = decode_tile(next_tile, a.tiles_m, a.tiles_n);
       set_sources(t);
-      issue(I0{}, 0);
-      issue(I1{}, 1);
-      issue(I2{}, 2);
-      issue_ops(t, e ^ 1);
     }
     __builtin_amdgcn_sched_barrier(0);
-    epilogue(cur, e);
-    if (!more) return false;
-    return true;
+    epilogue(cur, e, more, t);
+    return more;
   };
   for (;;) {
     if (!tile_iter(std::integral_constant<int, 0>{})) break;
