@@ -10,6 +10,9 @@
 // the position-only tables across heads; each head costs two independent 16-byte loads of x
 // (plus gamma, an L1/L2 hit) and two 16-byte streaming stores.  inv_rms is folded into the gamma
 // multiply.  The two layouts differ only in how threads map to (token, head): see the kernels.
+// Blocks of 8 tokens (512 threads), ten heads' loads in flight per thread before their
+// stores, streaming loads and stores of x: the shape that moved the most bytes per second
+// in a sweep of block size, batch depth and cache policy on the in-place strided pattern.
 #include "device_common.h"
 #include "internal.h"
 
@@ -18,7 +21,7 @@ namespace qkvmx {
 namespace {
 
 constexpr int kThreadsPerToken = 64;
-constexpr int kTokensPerBlock = 4;
+constexpr int kTokensPerBlock = 8;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -62,7 +65,13 @@ __device__ __forceinline__ void load8f(const float* p, float (&f)[8]) {
 // One token's work for one thread: the 8-lane chunk j0 (and its rotate-half partners
 // j0 + d/2 ..) of the touched heads h = h0, h0 + hstep, ...; base_of(h, is_k) addresses the
 // head's d elements for this token.  The token's cos/sin values and inv_rms are loaded once and
-// reused for every head.
+// reused for every head.  Heads are taken kBatch at a time: the loads of a whole batch are
+// issued before any of its stores, so each block keeps its tokens' Q/K bytes in flight at once,
+// and both the loads and the stores of x are non-temporal (x is touched exactly once; with
+// both streaming, the in-place read-modify-write of the strided Q/K columns sustains a higher
+// DRAM rate than with cached accesses).  gamma and the tables are re-read by every token and
+// stay cached.
+constexpr int kBatch = 10;
 template <typename BaseOf>
 __device__ __forceinline__ void apply_token(const NormRopeArgs& a, int64_t token, int j0, int h0,
                                             int hstep, BaseOf base_of) {
@@ -79,37 +88,51 @@ __device__ __forceinline__ void apply_token(const NormRopeArgs& a, int64_t token
   float rq = 1.0f, rk = 1.0f;
   if (a.norm_q) rq = 1.0f / sqrtf(a.ssq[token * 2] / (float)(a.nq * a.d) + a.eps);
   if (a.norm_k) rk = 1.0f / sqrtf(a.ssq[token * 2 + 1] / (float)(a.nkv * a.d) + a.eps);
-#pragma unroll 4
-  for (int h = h0; h < a.heads; h += hstep) {
-    const bool is_k = h >= a.heads_q;
-    uint16_t* base = base_of(h, is_k);
-    float lo[8], hi[8];
-    unpack8(*reinterpret_cast<const uint4*>(base + j0), lo);
-    unpack8(*reinterpret_cast<const uint4*>(base + half + j0), hi);
-    const bool norm = is_k ? a.norm_k : a.norm_q;
-    if (norm) {
-      const float r = is_k ? rk : rq;
-      const uint16_t* g = is_k ? a.gk + (int64_t)(h - a.heads_q) * a.d : a.gq + (int64_t)h * a.d;
-      float glo[8], ghi[8];
-      unpack8(*reinterpret_cast<const uint4*>(g + j0), glo);
-      unpack8(*reinterpret_cast<const uint4*>(g + half + j0), ghi);
+  for (int hb = h0; hb < a.heads; hb += kBatch * hstep) {
+    u32x4 xlo[kBatch], xhi[kBatch];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        lo[e] = lo[e] * (glo[e] * r);
-        hi[e] = hi[e] * (ghi[e] * r);
+    for (int b = 0; b < kBatch; ++b) {
+      const int h = hb + b * hstep;
+      if (h < a.heads) {
+        const uint16_t* base = base_of(h, h >= a.heads_q);
+        xlo[b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + j0));
+        xhi[b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + half + j0));
       }
     }
-    if (a.rope) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float ol = lo[e] * clo[e] - hi[e] * slo[e];
-        const float oh = hi[e] * chi[e] + lo[e] * shi[e];
-        lo[e] = ol;
-        hi[e] = oh;
+    for (int b = 0; b < kBatch; ++b) {
+      const int h = hb + b * hstep;
+      if (h >= a.heads) break;
+      const bool is_k = h >= a.heads_q;
+      uint16_t* base = base_of(h, is_k);
+      float lo[8], hi[8];
+      unpack8(make_uint4(xlo[b].x, xlo[b].y, xlo[b].z, xlo[b].w), lo);
+      unpack8(make_uint4(xhi[b].x, xhi[b].y, xhi[b].z, xhi[b].w), hi);
+      const bool norm = is_k ? a.norm_k : a.norm_q;
+      if (norm) {
+        const float r = is_k ? rk : rq;
+        const uint16_t* g = is_k ? a.gk + (int64_t)(h - a.heads_q) * a.d : a.gq + (int64_t)h * a.d;
+        float glo[8], ghi[8];
+        unpack8(*reinterpret_cast<const uint4*>(g + j0), glo);
+        unpack8(*reinterpret_cast<const uint4*>(g + half + j0), ghi);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          lo[e] = lo[e] * (glo[e] * r);
+          hi[e] = hi[e] * (ghi[e] * r);
+        }
       }
+      if (a.rope) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float ol = lo[e] * clo[e] - hi[e] * slo[e];
+          const float oh = hi[e] * chi[e] + lo[e] * shi[e];
+          lo[e] = ol;
+          hi[e] = oh;
+        }
+      }
+      __builtin_nontemporal_store(pack8(lo), reinterpret_cast<u32x4*>(base + j0));
+      __builtin_nontemporal_store(pack8(hi), reinterpret_cast<u32x4*>(base + half + j0));
     }
-    __builtin_nontemporal_store(pack8(lo), reinterpret_cast<u32x4*>(base + j0));
-    __builtin_nontemporal_store(pack8(hi), reinterpret_cast<u32x4*>(base + half + j0));
   }
 }
 
