@@ -120,6 +120,30 @@ qkvmx_status rmsnorm_mx_quantize(const uint16_t* hidden, const uint16_t* residua
                                  int64_t unpadded_H, uint16_t* residual_out, uint8_t* packed_out,
                                  hipStream_t stream);
 
+/* MX block-32 encoding of activation rows ([RMSNORM-MX] qmx_output_dtype: E4M3 codes with one
+ * E8M0 scale per 32 elements of a row; the other machine's packing and swizzle of the scales are
+ * not reproduced).  x: [T, H] fp32 or bf16 (x_dtype).  codes_out: [T, H] bytes, natural H order;
+ * e8m0_out: [T, H / 32] bytes, byte b of row t the exponent of elements [32 b, 32 b + 32).
+ * Per block: E = clamp(floor(log2(max |x| of the block)) - 8 + 127, 0, 254), codes = E4M3
+ * round-to-nearest-even saturating of x / 2^(E - 127) (the rule the weight encoder uses); an
+ * all-zero block stores E = 0 and zero codes.  Requires H % 32 == 0, H <= 16384; x 16-byte,
+ * codes_out 8-byte, e8m0_out 4-byte aligned. */
+qkvmx_status mx_block_quantize(const void* x, int32_t x_dtype, int64_t T, int64_t H,
+                               uint8_t* codes_out, uint8_t* e8m0_out, hipStream_t stream);
+
+/* Fused residual add + RMSNorm + MX block-32 quantisation ([RMSNORM-MX]: residual, eps,
+ * unpadded_hidden_size, qmx_output_dtype, emit_norm_bf16).  r, inv and y are those of
+ * rmsnorm_mx_quantize; y is then encoded as mx_block_quantize does, and when norm_out is not
+ * NULL y is also stored there rounded to bf16 (round to nearest even): emit_norm_bf16.
+ * hidden, residual, residual_out, norm_out: [T, H] bf16; gamma: [H] bf16; codes_out [T, H];
+ * e8m0_out [T, H / 32].  residual_out is required iff residual is given.  Requires H % 32 == 0,
+ * H <= 16384; bf16 tensors 16-byte, codes_out 8-byte, e8m0_out 4-byte aligned. */
+qkvmx_status rmsnorm_mx_block_quantize(const uint16_t* hidden, const uint16_t* residual,
+                                       const uint16_t* gamma, float eps, int64_t T, int64_t H,
+                                       int64_t unpadded_H, uint16_t* residual_out,
+                                       uint8_t* codes_out, uint8_t* e8m0_out, uint16_t* norm_out,
+                                       hipStream_t stream);
+
 /* ------------------------------------------------------------------------------------------
  * Pass 1: the projection ([QKV-CTE] "Upstream behavior", O[S, I] = A[S, H] @ W[H, I] + bias,
  * I = (num_heads + 2 * num_kv_heads) * head_dim; "Design 1)" step a).
@@ -155,6 +179,28 @@ qkvmx_status qkv_rowmx_project(const uint8_t* a_codes, int64_t a_row_stride,
                                int32_t num_kv_heads, int32_t head_dim, int32_t layout,
                                uint16_t* out, float* ssq, void* workspace, size_t ws_bytes,
                                hipStream_t stream);
+
+/* Workspace bytes qkv_mx_project needs (the per-tile sums of squares and the tile counters;
+ * the activation stages are read straight from the rows).  0 for invalid sizes. */
+size_t qkv_mx_workspace_bytes(int64_t T, int64_t H, int64_t I);
+
+/* Pass 1 on MX block-32 activations ([RMSNORM-MX] qmx_output_dtype feeding [QKV-CTE]'s
+ * projection): as qkv_rowmx_project with the row scale replaced by per-block exponents,
+ * out[t, i] = bf16_RNE( c[i] * sum_h dec(a[t, h]) * 2^(Ea[t, h/32] - 127)
+ *                                  * dec(W[h, i]) * 2^(E[h/32, i] - 127) + bias[i] ),
+ * and ssq as there (fp32 values before rounding; V excluded).
+ *   a_codes   E4M3 codes of row t at a_codes + t * a_row_stride (H bytes).
+ *   a_e8m0    E8M0 exponents of row t at a_e8m0 + t * a_e8m0_stride (H / 32 bytes).
+ *   workspace >= qkv_mx_workspace_bytes(T, H, I) bytes, 256-byte aligned, required; scratch.
+ * Other arguments, layouts and errors as qkv_rowmx_project.  Requires H % 256 == 0
+ * (QKVMX_ERR_UNSUPPORTED otherwise), a_row_stride >= H and a multiple of 16, a_codes 16-byte
+ * aligned, a_e8m0_stride >= H / 32 and a multiple of 4, a_e8m0 4-byte aligned. */
+qkvmx_status qkv_mx_project(const uint8_t* a_codes, int64_t a_row_stride, const uint8_t* a_e8m0,
+                            int64_t a_e8m0_stride, const void* w_packed,
+                            const float* w_channel_scale, const uint16_t* bias, int64_t T,
+                            int64_t H, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t layout, uint16_t* out, float* ssq, void* workspace,
+                            size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * Pass 2: across-heads RMSNorm + rotate-half RoPE, in place on Q and K; V is neither read nor

@@ -20,7 +20,8 @@ __all__ = [
     "NORM_Q", "NORM_K", "FUSED_ROPE", "LAYOUT_BSD", "LAYOUT_NBSD", "DTYPE_F32", "DTYPE_BF16", "QkvmxError",
     "lib", "lib_path", "mx_weight_quantize", "qkv_weight_packed_bytes", "qkv_weight_prepack",
     "row_quantize_packed", "rmsnorm_mx_quantize", "qkvmx_workspace_bytes", "qkv_rowmx_project",
-    "qk_norm_rope_apply", "prepare_weight",
+    "qk_norm_rope_apply", "prepare_weight", "mx_block_quantize", "rmsnorm_mx_block_quantize",
+    "qkv_mx_workspace_bytes", "qkv_mx_project",
 ]
 
 
@@ -89,6 +90,47 @@ def rmsnorm_mx_quantize(hidden, gamma, eps: float, packed_out, residual=None, re
     _check(lib().rmsnorm_mx_quantize(_ptr(hidden), _ptr(residual), _ptr(gamma), float(eps), T, H,
                                      unpadded_h, _ptr(residual_out), _ptr(packed_out),
                                      _stream(stream)), "rmsnorm_mx_quantize")
+
+
+def mx_block_quantize(x, codes_out, e8m0_out, stream=None):
+    """x [T, H] fp32 or bf16 -> MX block-32 codes [T, H] uint8 and E8M0 exponents [T, H // 32]."""
+    import torch
+    T, H = x.shape
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise QkvmxError("mx_block_quantize takes fp32 or bf16 rows")
+    dt = DTYPE_BF16 if x.dtype == torch.bfloat16 else DTYPE_F32
+    _check(lib().mx_block_quantize(_ptr(x), dt, T, H, _ptr(codes_out), _ptr(e8m0_out),
+                                   _stream(stream)), "mx_block_quantize")
+
+
+def rmsnorm_mx_block_quantize(hidden, gamma, eps: float, codes_out, e8m0_out, residual=None,
+                              residual_out=None, norm_out=None, unpadded_h: int = 0,
+                              stream=None):
+    """bf16 hidden [T, H] (+ residual) -> residual_out, MX block-32 codes / exponents and
+    (norm_out) the bf16 normed rows."""
+    T, H = hidden.shape
+    _check(lib().rmsnorm_mx_block_quantize(_ptr(hidden), _ptr(residual), _ptr(gamma), float(eps),
+                                           T, H, unpadded_h, _ptr(residual_out), _ptr(codes_out),
+                                           _ptr(e8m0_out), _ptr(norm_out), _stream(stream)),
+           "rmsnorm_mx_block_quantize")
+
+
+def qkv_mx_workspace_bytes(T: int, H: int, I: int) -> int:
+    return int(lib().qkv_mx_workspace_bytes(T, H, I))
+
+
+def qkv_mx_project(a_codes, a_e8m0, w_packed, out, *, H: int, num_heads: int, num_kv_heads: int,
+                   head_dim: int, channel_scale=None, bias=None, ssq=None, workspace=None,
+                   layout: int = LAYOUT_BSD, stream=None):
+    """Pass 1 on MX block-32 activations: codes [T, stride >= H] and exponents
+    [T, stride >= H / 32] (row strides taken from the tensors' shapes)."""
+    T = a_codes.shape[0]
+    ws_ptr, ws_n = (None, 0) if workspace is None else (_ptr(workspace),
+                                                        workspace.numel() * workspace.element_size())
+    _check(lib().qkv_mx_project(_ptr(a_codes), a_codes.shape[1], _ptr(a_e8m0), a_e8m0.shape[1],
+                                _ptr(w_packed), _ptr(channel_scale), _ptr(bias), T, H, num_heads,
+                                num_kv_heads, head_dim, layout, _ptr(out), _ptr(ssq), ws_ptr,
+                                ws_n, _stream(stream)), "qkv_mx_project")
 
 
 def qkvmx_workspace_bytes(T: int, H: int, I: int) -> int:

@@ -65,6 +65,14 @@ inline size_t counters_offset(int64_t T, int64_t H, int64_t I) {
 inline size_t workspace_total_bytes(int64_t T, int64_t H, int64_t I) {
   return counters_offset(T, H, I) + kCounterBytes;
 }
+// MX-activation projection workspace (the activation stages are read from the rows): the
+// sum-of-squares partials [P][T][2] fp32, then the 256-byte counter block.
+inline size_t mx_counters_offset(int64_t T, int64_t I) {
+  return (partials_bytes(T, I) + 255) / 256 * 256;
+}
+inline size_t mx_workspace_total_bytes(int64_t T, int64_t I) {
+  return mx_counters_offset(T, I) + kCounterBytes;
+}
 
 hipError_t launch_mx_weight_quantize(const float* w, int64_t H, int64_t I, uint8_t* codes,
                                      uint8_t* e8m0, hipStream_t s);
@@ -80,6 +88,16 @@ hipError_t launch_project(const uint8_t* a_codes, int64_t a_stride, const uint8_
                           const uint16_t* bias, int64_t T, int64_t H, int64_t I, int64_t Iq,
                           int64_t Ik, int64_t d, bool nbsd, uint16_t* out, float* ssq,
                           uint8_t* ws, hipStream_t s);
+hipError_t launch_project_mx(const uint8_t* a_codes, int64_t a_stride, const uint8_t* a_e8,
+                             int64_t e_stride, const uint8_t* w_packed, const float* chan_scale,
+                             const uint16_t* bias, int64_t T, int64_t H, int64_t I, int64_t Iq,
+                             int64_t Ik, int64_t d, bool nbsd, uint16_t* out, float* ssq,
+                             uint8_t* ws, hipStream_t s);
+hipError_t launch_mx_quantize(const void* x, int dtype, int64_t T, int64_t H, uint8_t* codes,
+                              uint8_t* e8, hipStream_t s);
+hipError_t launch_rmsnorm_mx(const uint16_t* hid, const uint16_t* res, const uint16_t* gamma,
+                             float eps, int64_t T, int64_t H, int64_t Hu, uint16_t* res_out,
+                             uint8_t* codes, uint8_t* e8, uint16_t* norm_out, hipStream_t s);
 hipError_t launch_norm_rope(uint16_t* qkv, const float* ssq, const uint16_t* q_gamma,
                             const uint16_t* k_gamma, const float* cos_tab, const float* sin_tab,
                             int64_t T, int nq, int nkv, int d, float eps, uint32_t flags,

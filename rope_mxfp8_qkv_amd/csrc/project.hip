@@ -71,7 +71,9 @@ struct ProjectArgs {
   int64_t s_stride;
   const uint8_t* w_img;        // [NT][KS][16 KiB]
   const uint8_t* w_scales;     // [KS / 4][NT * 256][2] dwords
-  const uint8_t* x_img;        // activation stage images [MT][KS][16 KiB] (workspace)
+  const uint8_t* x_img;        // activation stage images [MT][KS][16 KiB] (workspace; ROW_MX)
+  const uint8_t* x_e8;         // MX block-32 activations: E8M0 exponents, row t at t * e_stride
+  int64_t e_stride;
   const float* chan_scale;     // [I] or null
   const uint16_t* bias;        // [I] or null
   int64_t T, H, I, Iq, Ik;
@@ -112,6 +114,15 @@ __device__ __forceinline__ void dma16_blk(uint32_t base, const uint8_t* sbase, u
     default: QKVMX_DMA_BLK(3072); break;
   }
 #undef QKVMX_DMA_BLK
+}
+// 1 KiB block I of a stage straight from activation rows: lane L reads sbase + voff_L (a row
+// chunk of its own) and writes LDS at the stage buffer + 1024 I + 16 L; the LDS offset rides in
+// M0, the global address carries no immediate.
+template <int Q, int I>
+__device__ __forceinline__ void dma16_row(uint32_t base, const uint8_t* sbase, uint32_t voff) {
+  asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(base), "v"(voff), "s"(sbase), "n"(Q * kStageImage + 1024 * I)
+               : "memory", "m0", "scc");
 }
 // Dword DMA from a per-lane 64-bit address (lane L: 4 bytes from g_L to LDS lds + 4 L).
 __device__ __forceinline__ void dma4g(uint32_t lds, const void* g) {
@@ -159,11 +170,17 @@ __device__ __forceinline__ Tile decode_tile(int tile, int tiles_m, int tiles_n) 
   return Tile{first_m + in_group % gm, in_group / gm};
 }
 
-template <bool kChanScale, bool kBias, bool kNbsd>
+// kMx: MX block-32 activations (E4M3 rows with one E8M0 exponent per 32 elements).  The rows
+// are 16-byte aligned, so the activation stages are DMA-copied straight from them (no per-call
+// stage images); their exponents feed the MFMA's B-scale as the weight's feed the A-scale, and
+// the epilogue has no row scale.
+template <bool kChanScale, bool kBias, bool kNbsd, bool kMx>
 __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_w[kBufs][kStageImage];
   __shared__ __attribute__((aligned(16))) uint8_t lds_x[kBufs][kStageImage];
   __shared__ __attribute__((aligned(16))) uint8_t lds_sc[2][kTileN * 8];
+  // MX: activation exponents of a superstep, [token][8 bytes] in row order (2 ring slots)
+  __shared__ __attribute__((aligned(16))) uint8_t lds_xsc[kMx ? 2 : 1][kMx ? kTileM * 8 : 16];
   // epilogue operands, double-buffered (the next tile's arrive while the current tile's are
   // in use): channel scale and row scale (fp32) and the bias, DMA-copied as raw bf16 pairs and
   // widened to fp32 at the start of the tile
@@ -211,20 +228,63 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   // ---- DMA sources of the current tile (wave-uniform bases, in SGPRs) ----
   // weight: wave w copies 1 KiB blocks 4 w .. 4 w + 3 of each 16 KiB stage image;
   // exponents: each wave copies 512 bytes (two dword DMAs) of the 2 KiB per superstep;
-  // activation: same scheme as the weight, from the per-call stage images
+  // activation: same scheme as the weight, from the per-call stage images (ROW_MX), or
+  // straight from the rows (MX: lane L of block i copies its own 16-byte chunk, the logical
+  // chunk (L % 4) ^ stage_swizzle(row) of row 64 w + 16 i + L / 4, rows past T clamped to the
+  // last one; xv[i] is that chunk's byte offset in the codes, xsv[j] the offset of exponent
+  // dword 128 w + 64 j + L of the tile's [256 tokens][8 bytes] per superstep)
   const uint32_t wdst = lds_addr(&lds_w[0][0]) + wave * 4096;
   const uint32_t xdst = lds_addr(&lds_x[0][0]) + wave * 4096;
   const uint32_t sdst = lds_addr(&lds_sc[0][0]) + wave * 512;
+  const uint32_t xsdst = lds_addr(&lds_xsc[0][0]) + wave * 512;
   const int64_t s_step = (int64_t)a.tiles_n * kTileN * 2 * 4;       // bytes per superstep
   const uint8_t* wbase;
   const uint8_t* xbase;
   const uint8_t* sbase;
+  uint32_t xv[4] = {0u, 0u, 0u, 0u}, xsv[2] = {0u, 0u};
   auto set_sources = [&](Tile u) {
     wbase = a.w_img + ((int64_t)u.tn * a.KS) * kStageImage + wave * 4096;
     sbase = a.w_scales + ((int64_t)u.tn * kTileN * 2) * 4 + wave * 512;
-    xbase = a.x_img + ((int64_t)u.tm * a.KS) * kStageImage + wave * 4096;
+    if (kMx) {
+      xbase = a.a_codes;
+      const int lv = fresh_lane();
+      const int64_t m0 = (int64_t)u.tm * kTileM;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wave * 64 + 16 * i + (lv >> 2);
+        const int c = (lv & 3) ^ stage_swizzle(row);
+        xv[i] = (uint32_t)(min(m0 + row, a.T - 1) * a.a_stride + 16 * c);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int d = wave * 128 + 64 * j + lv;
+        xsv[j] = (uint32_t)(min(m0 + (d >> 1), a.T - 1) * a.e_stride + 4 * (d & 1));
+      }
+    } else {
+      xbase = a.x_img + ((int64_t)u.tm * a.KS) * kStageImage + wave * 4096;
+    }
   };
   set_sources(t);
+
+  // activation DMA of 1 KiB block i of stage t (Q = t % 4)
+  auto xdma = [&](auto q_c, int t, uint32_t voff16, int i) __attribute__((always_inline)) {
+    constexpr int Q = decltype(q_c)::value;
+    if (kMx) {
+      const uint8_t* const src = xbase + (int64_t)t * kStage;
+      switch (i) {
+        case 0: dma16_row<Q, 0>(xdst, src, xv[0]); break;
+        case 1: dma16_row<Q, 1>(xdst, src, xv[1]); break;
+        case 2: dma16_row<Q, 2>(xdst, src, xv[2]); break;
+        default: dma16_row<Q, 3>(xdst, src, xv[3]); break;
+      }
+    } else {
+      dma16_blk<Q>(xdst, xbase + (int64_t)t * kStageImage, voff16, i);
+    }
+  };
+  // MX: exponent dword j of superstep sup into ring slot sup % 2
+  auto xsdma = [&](int64_t sup, int j) __attribute__((always_inline)) {
+    dma4(xsdst + (uint32_t)(sup & 1) * 2048 + 256 * j, a.x_e8 + sup * 8, xsv[j]);
+  };
 
   // DMA of stage t (t % 4 == Q) into buffer Q; a stage opening a superstep also brings that
   // superstep's exponents into ring slot (t / 4) % 2.
@@ -237,13 +297,16 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
       const uint32_t slot = sdst + (uint32_t)(sup & 1) * 2048;
       dma4(slot, sbase + sup * s_step, voff4);
       dma4(slot + 256, sbase + sup * s_step + 256, voff4);
+      if (kMx) {
+        xsdma(sup, 0);
+        xsdma(sup, 1);
+      }
     }
     const uint8_t* const wsrc_t = wbase + (int64_t)t * kStageImage;
-    const uint8_t* const xsrc_t = xbase + (int64_t)t * kStageImage;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       dma16_blk<Q>(wdst, wsrc_t, voff16, i);
-      dma16_blk<Q>(xdst, xsrc_t, voff16, i);
+      xdma(q_c, t, voff16, i);
     }
   };
 
@@ -253,8 +316,10 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   // 128 bf16 pairs of the tile's bias.
   auto issue_ops = [&](Tile u, int e) {
     const int lv = fresh_lane();
-    const int64_t m = min((int64_t)u.tm * kTileM + wave * 64 + lv, a.T - 1);
-    dma4g(lds_addr(&lds_sa[e][wave * 64]), a.a_scales + m * a.s_stride);
+    if (!kMx) {
+      const int64_t m = min((int64_t)u.tm * kTileM + wave * 64 + lv, a.T - 1);
+      dma4g(lds_addr(&lds_sa[e][wave * 64]), a.a_scales + m * a.s_stride);
+    }
     if (kChanScale) {
       const int64_t n = min((int64_t)u.tn * kTileN + wave * 64 + lv, a.I - 1);
       dma4g(lds_addr(&lds_cs[e][wave * 64]), a.chan_scale + n);
@@ -280,8 +345,8 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
 
   // lane-derived LDS offsets of the K-steps, recomputed at the start of every tile (from a
   // fresh lane index) so that none of them is live across the epilogue
-  int rw0, rw1, rx0, rx1, rsc;
-  uint32_t kvoff16;
+  int rw0, rw1, rx0, rx1, rsc, rxs;
+  uint32_t kvoff16, xsel;
   auto set_lane_offsets = [&]() {
     const int lv = fresh_lane();
     const int g = lv >> 5;
@@ -293,12 +358,16 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     rw0 = lds_off(w_row0, g); rw1 = lds_off(w_row0, 2 + g);
     rx0 = lds_off(x_row0, g); rx1 = lds_off(x_row0, 2 + g);
     rsc = (w_row0 * 2 + g) * 4;         // + 32 * 8 cf: this lane's exponent dword
+    // MX: this lane's token's 8 exponent bytes (+ 32 * 8 tf); byte q of the B-scale operand of
+    // K-step q must be the exponent of K-block 2 q + g of the superstep
+    rxs = x_row0 * 8;
+    xsel = 0x06040200u + 0x01010101u * (uint32_t)g;
     kvoff16 = lv * 16;
   };
 
   v16f acc[4][4];
   v8i wf[2][4], xf[2][4];
-  uint32_t sc[2][4];
+  uint32_t sc[2][4], xs[2][4];
   auto fload = [&](int buf, v8i (&wd)[4], v8i (&xd)[4]) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
@@ -316,6 +385,15 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
 #pragma unroll
     for (int cf = 0; cf < 4; ++cf)
       sd[cf] = *reinterpret_cast<const uint32_t*>(&lds_sc[slot][rsc + 256 * cf]);
+  };
+  auto xsload = [&](int slot, uint32_t (&xd)[4]) {
+    if (kMx) {
+#pragma unroll
+      for (int tf = 0; tf < 4; ++tf) {
+        const uint2 v = *reinterpret_cast<const uint2*>(&lds_xsc[slot][rxs + 256 * tf]);
+        xd[tf] = __builtin_amdgcn_perm(v.y, v.x, xsel);
+      }
+    }
   };
 
   // ---- software pipeline over K-steps of 64 bytes ----
@@ -342,13 +420,12 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     constexpr int nb = (q + 1) & (kBufs - 1);      // buffer of stage s + 1 (s % 4 == q)
     const int t = s + 4;                           // stage requested by this step
     const uint8_t* const wsrc_t = wbase + (int64_t)t * kStageImage;
-    const uint8_t* const xsrc_t = xbase + (int64_t)t * kStageImage;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int cf = k >> 2, tf = k & 3;
       acc[cf][tf] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          wf[p][cf], xf[p][tf], from_zero ? v16f{} : acc[cf][tf], 0, 0, q, (int)sc[0][cf], 0,
-          0x7F7F7F7F);
+          wf[p][cf], xf[p][tf], from_zero ? v16f{} : acc[cf][tf], 0, 0, q, (int)sc[0][cf],
+          kMx ? q : 0, kMx ? (int)xs[0][tf] : 0x7F7F7F7F);
       // fragment k / 2 of stage s + 1: even k -> weight fragment, odd k -> activation fragment
       const int f = k >> 2, half = (k >> 1) & 1;
       if ((k & 1) == 0) {
@@ -366,19 +443,26 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
           if ((k & 1) == 0)
             dma16_blk<q>(wdst, wsrc_t, kvoff16, i);
           else
-            dma16_blk<q>(xdst, xsrc_t, kvoff16, i);
+            xdma(q_c, t, kvoff16, i);
         } else if (q == 0 && (k == 8 || k == 9)) {
           const int64_t sup = t >> 2;
           const uint32_t slot = sdst + (uint32_t)(sup & 1) * 2048;
           dma4(slot + (k - 8) * 256, sbase + sup * s_step + (k - 8) * 256, kvoff16 >> 2);
+        } else if (kMx && q == 0 && (k == 10 || k == 11)) {
+          xsdma(t >> 2, k - 10);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     if (q == 3) {
       sload(((s >> 2) + 1) & 1, sc[1]);
+      xsload(((s >> 2) + 1) & 1, xs[1]);
 #pragma unroll
       for (int cf = 0; cf < 4; ++cf) sc[0][cf] = sc[1][cf];
+      if (kMx) {
+#pragma unroll
+        for (int tf = 0; tf < 4; ++tf) xs[0][tf] = xs[1][tf];
+      }
     }
     if (nwait >= 0) wait_vm<(nwait < 0 ? 0 : nwait)>();
     __syncthreads();
@@ -456,7 +540,7 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
       }
       // this pass's operands to registers first, under one LDS wait: the row scale of this
       // lane's token and the bias (and channel scale) of its 16 channel quads
-      const float sa = lds_sa[e][wm * 128 + tf * 32 + fr];
+      const float sa = kMx ? 1.0f : lds_sa[e][wm * 128 + tf * 32 + fr];
 #pragma unroll
       for (int cf = 0; cf < 4; ++cf) {
         float4 bq[1][4], cq[1][4];
@@ -573,6 +657,7 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     set_lane_offsets();
     fload(0, wf[0], xf[0]);
     sload(0, sc[0]);
+    xsload(0, xs[0]);
     __syncthreads();
     // the trip count is re-read through an opaque copy each tile: a loop-invariant test hoisted
     // out of the tile loop would be kept in a register (or spilled) across the whole tile
@@ -655,18 +740,93 @@ __global__ void __launch_bounds__(256) act_repack_kernel(const uint8_t* __restri
   reinterpret_cast<uint4*>(img)[(tm * KS + t) * (kStageImage / 16) + p] = o;
 }
 
-// ssq[t] = sum over partials p < P of ws[p][t] (fixed order); P = 0 gives zeros.
-__global__ void __launch_bounds__(256) ssq_reduce_kernel(const float* __restrict__ ws, int64_t P,
-                                                         int64_t T, float* __restrict__ ssq) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T) return;
+// Clears the per-XCD tile counters (the MX path has no repack kernel to do it).
+__global__ void counters_reset_kernel(unsigned* __restrict__ ctr) {
+  if (threadIdx.x < kXcds) ctr[threadIdx.x] = 0;
+}
+
+// ssq[t] = sum over partials p < P of ws[p][t]; P = 0 gives zeros.  A block covers 64 tokens
+// with 8 wavefronts: wavefront w adds the partials p = w, w + 8, ... of its lane's token in
+// increasing p (each load instruction reads 512 contiguous bytes), then wavefront 0 adds the
+// eight results in w order.  The order is fixed, so the sums are reproducible run to run.
+constexpr int kReduceWaves = 8;
+__global__ void __launch_bounds__(64 * kReduceWaves) ssq_reduce_kernel(const float* __restrict__ ws,
+                                                                       int64_t P, int64_t T,
+                                                                       float* __restrict__ ssq) {
+  __shared__ float2 part[kReduceWaves][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 64 + lane;
   float q = 0.f, k = 0.f;
-  for (int64_t p = 0; p < P; ++p) {
-    const float2 v = reinterpret_cast<const float2*>(ws)[p * T + t];
-    q += v.x;
-    k += v.y;
+  if (t < T) {
+#pragma unroll 4
+    for (int64_t p = w; p < P; p += kReduceWaves) {
+      const float2 v = reinterpret_cast<const float2*>(ws)[p * T + t];
+      q += v.x;
+      k += v.y;
+    }
   }
-  reinterpret_cast<float2*>(ssq)[t] = make_float2(q, k);
+  part[w][lane] = make_float2(q, k);
+  __syncthreads();
+  if (w == 0 && t < T) {
+    float2 r = part[0][lane];
+#pragma unroll
+    for (int i = 1; i < kReduceWaves; ++i) {
+      r.x += part[i][lane].x;
+      r.y += part[i][lane].y;
+    }
+    reinterpret_cast<float2*>(ssq)[t] = r;
+  }
+}
+
+}  // namespace
+
+namespace {
+
+// Persistent project_kernel launch (one block per compute unit, each walking its XCD's tile
+// range), then the fixed-order sum of the partials when ssq is requested.
+template <bool kMx>
+hipError_t launch_core(const ProjectArgs& a, bool chan, bool bias, bool nbsd, float* ssq,
+                       hipStream_t s) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n;
+  const unsigned nblocks = (unsigned)std::min<int64_t>(ntiles, std::max(cus, 1));
+  const dim3 grid(nblocks), block(kThreads);
+  const int variant = (chan ? 4 : 0) | (bias ? 2 : 0) | (nbsd ? 1 : 0);
+  switch (variant) {
+    case 0: hipLaunchKernelGGL((project_kernel<false, false, false, kMx>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((project_kernel<false, false, true, kMx>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((project_kernel<false, true, false, kMx>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((project_kernel<false, true, true, kMx>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((project_kernel<true, false, false, kMx>), grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL((project_kernel<true, false, true, kMx>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((project_kernel<true, true, false, kMx>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((project_kernel<true, true, true, kMx>), grid, block, 0, s, a); break;
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess || !ssq) return e;
+  // only the partials of 128-channel groups that overlap Q or K are written and summed
+  const int64_t P = ceil_div(a.Iq + a.Ik, (int64_t)kPartialN);
+  hipLaunchKernelGGL(ssq_reduce_kernel, dim3((unsigned)ceil_div(a.T, 64)),
+                     dim3(64 * kReduceWaves), 0, s, a.ws, P, a.T, ssq);
+  return hipGetLastError();
+}
+
+ProjectArgs common_args(const uint8_t* w_packed, const float* chan_scale, const uint16_t* bias,
+                        int64_t T, int64_t H, int64_t I, int64_t Iq, int64_t Ik, int64_t d,
+                        uint16_t* out) {
+  ProjectArgs a{};
+  a.w_img = w_packed;
+  a.w_scales = w_packed + packed_scales_offset(H, I);
+  a.chan_scale = chan_scale; a.bias = bias;
+  a.T = T; a.H = H; a.I = I; a.Iq = Iq; a.Ik = Ik; a.d = d;
+  a.KS = (int)packed_stages(H);
+  a.tiles_m = (int)ceil_div(T, kTileM);
+  a.tiles_n = (int)packed_tiles_n(I);
+  a.out = out;
+  return a;
 }
 
 }  // namespace
@@ -676,52 +836,35 @@ hipError_t launch_project(const uint8_t* a_codes, int64_t a_stride, const uint8_
                           const uint16_t* bias, int64_t T, int64_t H, int64_t I, int64_t Iq,
                           int64_t Ik, int64_t d, bool nbsd, uint16_t* out, float* ssq,
                           uint8_t* ws, hipStream_t s) {
-  ProjectArgs a;
+  ProjectArgs a = common_args(w_packed, chan_scale, bias, T, H, I, Iq, Ik, d, out);
   a.a_codes = a_codes; a.a_stride = a_stride; a.a_scales = a_scales; a.s_stride = s_stride;
-  a.w_img = w_packed;
-  a.w_scales = w_packed + packed_scales_offset(H, I);
   a.x_img = ws;
-  a.chan_scale = chan_scale; a.bias = bias;
-  a.T = T; a.H = H; a.I = I; a.Iq = Iq; a.Ik = Ik; a.d = d;
-  a.KS = (int)packed_stages(H);
-  a.tiles_m = (int)ceil_div(T, kTileM);
-  a.tiles_n = (int)packed_tiles_n(I);
-  a.out = out;
   float* partials = reinterpret_cast<float*>(ws + act_image_bytes(T, H));
   a.ws = ssq ? partials : nullptr;
-  dim3 rg(kStageImage / 16 / 256, (unsigned)a.KS, (unsigned)a.tiles_m);
   a.ctr = reinterpret_cast<unsigned*>(ws + counters_offset(T, H, I));
+  // the activation rows re-laid as stage images (this kernel also resets the tile counters)
+  dim3 rg(kStageImage / 16 / 256, (unsigned)a.KS, (unsigned)a.tiles_m);
   hipLaunchKernelGGL(act_repack_kernel, rg, dim3(256), 0, s, a_codes, a_stride, T, H, a.KS, ws,
                      a.ctr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // persistent blocks: one per compute unit (the kernel's LDS admits one block per CU), each
-  // walking its XCD's tile range
-  int dev = 0, cus = 0;
-  e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  return launch_core<false>(a, chan_scale, bias, nbsd, ssq, s);
+}
+
+hipError_t launch_project_mx(const uint8_t* a_codes, int64_t a_stride, const uint8_t* a_e8,
+                             int64_t e_stride, const uint8_t* w_packed, const float* chan_scale,
+                             const uint16_t* bias, int64_t T, int64_t H, int64_t I, int64_t Iq,
+                             int64_t Ik, int64_t d, bool nbsd, uint16_t* out, float* ssq,
+                             uint8_t* ws, hipStream_t s) {
+  ProjectArgs a = common_args(w_packed, chan_scale, bias, T, H, I, Iq, Ik, d, out);
+  a.a_codes = a_codes; a.a_stride = a_stride;
+  a.x_e8 = a_e8; a.e_stride = e_stride;
+  a.ws = ssq ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ctr = reinterpret_cast<unsigned*>(ws + mx_counters_offset(T, I));
+  hipLaunchKernelGGL(counters_reset_kernel, dim3(1), dim3(64), 0, s, a.ctr);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n;
-  const unsigned nblocks = (unsigned)std::min<int64_t>(ntiles, std::max(cus, 1));
-  const dim3 grid(nblocks), block(kThreads);
-  const int variant = (chan_scale ? 4 : 0) | (bias ? 2 : 0) | (nbsd ? 1 : 0);
-  switch (variant) {
-    case 0: hipLaunchKernelGGL((project_kernel<false, false, false>), grid, block, 0, s, a); break;
-    case 1: hipLaunchKernelGGL((project_kernel<false, false, true>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((project_kernel<false, true, false>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((project_kernel<false, true, true>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((project_kernel<true, false, false>), grid, block, 0, s, a); break;
-    case 5: hipLaunchKernelGGL((project_kernel<true, false, true>), grid, block, 0, s, a); break;
-    case 6: hipLaunchKernelGGL((project_kernel<true, true, false>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((project_kernel<true, true, true>), grid, block, 0, s, a); break;
-  }
-  e = hipGetLastError();
-  if (e != hipSuccess || !ssq) return e;
-  // only the partials of 128-channel groups that overlap Q or K are written and summed
-  const int64_t P = ceil_div(Iq + Ik, (int64_t)kPartialN);
-  hipLaunchKernelGGL(ssq_reduce_kernel, dim3((unsigned)ceil_div(T, 256)), dim3(256), 0, s,
-                     partials, P, T, ssq);
-  return hipGetLastError();
+  return launch_core<true>(a, chan_scale, bias, nbsd, ssq, s);
 }
 
 }  // namespace qkvmx

@@ -109,6 +109,38 @@ qkvmx_status rmsnorm_mx_quantize(const uint16_t* hidden, const uint16_t* residua
                                             packed_out, stream), "rmsnorm_mx_quantize");
 }
 
+qkvmx_status mx_block_quantize(const void* x, int32_t x_dtype, int64_t T, int64_t H,
+                               uint8_t* codes_out, uint8_t* e8m0_out, hipStream_t stream) {
+  if (!x || !codes_out || !e8m0_out) return fail(QKVMX_ERR_NULL, "mx_block_quantize: null pointer");
+  if (x_dtype != QKVMX_DTYPE_F32 && x_dtype != QKVMX_DTYPE_BF16) return fail(QKVMX_ERR_ARG, "mx_block_quantize: bad dtype");
+  if (T <= 0 || H <= 0 || H % 32) return fail(QKVMX_ERR_SHAPE, "mx_block_quantize: need T > 0, H %% 32 == 0");
+  if (H > kMaxRowH) return fail(QKVMX_ERR_UNSUPPORTED, "mx_block_quantize: H > %lld", (long long)kMaxRowH);
+  if (!aligned(x, 16) || !aligned(codes_out, 8) || !aligned(e8m0_out, 4))
+    return fail(QKVMX_ERR_ALIGN, "mx_block_quantize: x 16-byte, codes 8-byte, exponents 4-byte aligned");
+  return hip_status(launch_mx_quantize(x, x_dtype, T, H, codes_out, e8m0_out, stream), "mx_block_quantize");
+}
+
+qkvmx_status rmsnorm_mx_block_quantize(const uint16_t* hidden, const uint16_t* residual,
+                                       const uint16_t* gamma, float eps, int64_t T, int64_t H,
+                                       int64_t unpadded_H, uint16_t* residual_out,
+                                       uint8_t* codes_out, uint8_t* e8m0_out, uint16_t* norm_out,
+                                       hipStream_t stream) {
+  if (!hidden || !gamma || !codes_out || !e8m0_out) return fail(QKVMX_ERR_NULL, "rmsnorm_mx_block_quantize: null pointer");
+  if (residual && !residual_out) return fail(QKVMX_ERR_ARG, "rmsnorm_mx_block_quantize: residual_out is required with a residual");
+  if (!residual && residual_out) return fail(QKVMX_ERR_ARG, "rmsnorm_mx_block_quantize: residual_out given without a residual");
+  if (T <= 0 || H <= 0 || H % 32) return fail(QKVMX_ERR_SHAPE, "rmsnorm_mx_block_quantize: need T > 0, H %% 32 == 0");
+  if (unpadded_H < 0 || unpadded_H > H) return fail(QKVMX_ERR_SHAPE, "rmsnorm_mx_block_quantize: unpadded_H outside [0, H]");
+  if (!(eps >= 0.0f)) return fail(QKVMX_ERR_ARG, "rmsnorm_mx_block_quantize: eps must be >= 0");
+  if (H > kMaxRowH) return fail(QKVMX_ERR_UNSUPPORTED, "rmsnorm_mx_block_quantize: H > %lld", (long long)kMaxRowH);
+  if (!aligned(hidden, 16) || !aligned(gamma, 16) || (residual && !aligned(residual, 16)) ||
+      (residual_out && !aligned(residual_out, 16)) || (norm_out && !aligned(norm_out, 16)) ||
+      !aligned(codes_out, 8) || !aligned(e8m0_out, 4))
+    return fail(QKVMX_ERR_ALIGN, "rmsnorm_mx_block_quantize: bf16 tensors 16-byte, codes 8-byte, exponents 4-byte aligned");
+  const int64_t Hu = unpadded_H ? unpadded_H : H;
+  return hip_status(launch_rmsnorm_mx(hidden, residual, gamma, eps, T, H, Hu, residual_out,
+                                      codes_out, e8m0_out, norm_out, stream), "rmsnorm_mx_block_quantize");
+}
+
 size_t qkvmx_workspace_bytes(int64_t T, int64_t H, int64_t I) {
   if (T <= 0 || H <= 0 || I <= 0 || H % 32) return 0;
   return workspace_total_bytes(T, H, I);
@@ -149,6 +181,48 @@ qkvmx_status qkv_rowmx_project(const uint8_t* a_codes, int64_t a_row_stride,
                                    (const uint8_t*)w_packed, w_channel_scale, bias, T, H, I, Iq,
                                    Ik, head_dim, layout == QKVMX_LAYOUT_NBSD, out, ssq,
                                    (uint8_t*)workspace, stream), "qkv_rowmx_project");
+}
+
+size_t qkv_mx_workspace_bytes(int64_t T, int64_t H, int64_t I) {
+  if (T <= 0 || H <= 0 || I <= 0 || H % 32) return 0;
+  return mx_workspace_total_bytes(T, I);
+}
+
+qkvmx_status qkv_mx_project(const uint8_t* a_codes, int64_t a_row_stride, const uint8_t* a_e8m0,
+                            int64_t a_e8m0_stride, const void* w_packed,
+                            const float* w_channel_scale, const uint16_t* bias, int64_t T,
+                            int64_t H, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t layout, uint16_t* out, float* ssq, void* workspace,
+                            size_t ws_bytes, hipStream_t stream) {
+  if (!a_codes || !a_e8m0 || !w_packed || !out) return fail(QKVMX_ERR_NULL, "qkv_mx_project: null pointer");
+  if (!workspace) return fail(QKVMX_ERR_WORKSPACE, "qkv_mx_project: workspace is required");
+  if (T <= 0 || H <= 0 || H % 32) return fail(QKVMX_ERR_SHAPE, "qkv_mx_project: need T > 0, H %% 32 == 0");
+  if (H % 256)
+    return fail(QKVMX_ERR_UNSUPPORTED, "qkv_mx_project: needs H %% 256 == 0 (activation stages are read straight from the rows)");
+  if (num_heads < 1 || num_kv_heads < 0 || head_dim <= 0 || head_dim % 16)
+    return fail(QKVMX_ERR_SHAPE, "qkv_mx_project: need num_heads >= 1, num_kv_heads >= 0, head_dim %% 16 == 0");
+  if (layout != QKVMX_LAYOUT_BSD && layout != QKVMX_LAYOUT_NBSD)
+    return fail(QKVMX_ERR_ARG, "qkv_mx_project: layout must be QKVMX_LAYOUT_BSD or QKVMX_LAYOUT_NBSD");
+  if (a_row_stride < H || a_row_stride % 16 || a_e8m0_stride < H / 32 || a_e8m0_stride % 4)
+    return fail(QKVMX_ERR_SHAPE, "qkv_mx_project: a_row_stride >= H and a multiple of 16, a_e8m0_stride >= H / 32 and a multiple of 4");
+  const int64_t I = (int64_t)(num_heads + 2 * (int64_t)num_kv_heads) * head_dim;
+  if ((T - 1) * a_row_stride + H >= kMaxOffset || (T - 1) * a_e8m0_stride + H / 32 >= kMaxOffset)
+    return fail(QKVMX_ERR_UNSUPPORTED, "qkv_mx_project: activation spans must be < 2^31 bytes");
+  if (I * 2 * 256 >= kMaxOffset)
+    return fail(QKVMX_ERR_UNSUPPORTED, "qkv_mx_project: I must be < 2^22");
+  if (layout == QKVMX_LAYOUT_NBSD && 2 * ((256 + (int64_t)head_dim) * T + 257 * (int64_t)head_dim) >= kMaxOffset)
+    return fail(QKVMX_ERR_UNSUPPORTED, "qkv_mx_project: NBSd needs 2 ((256 + head_dim) T + 257 head_dim) < 2^31");
+  if (ws_bytes < mx_workspace_total_bytes(T, I))
+    return fail(QKVMX_ERR_WORKSPACE, "qkv_mx_project: workspace %zu < %zu bytes", ws_bytes, mx_workspace_total_bytes(T, I));
+  if (!aligned(a_codes, 16) || !aligned(a_e8m0, 4) || !aligned(w_packed, 256) ||
+      (w_channel_scale && !aligned(w_channel_scale, 16)) || (bias && !aligned(bias, 8)) ||
+      !aligned(out, 16) || (ssq && !aligned(ssq, 8)) || !aligned(workspace, 256))
+    return fail(QKVMX_ERR_ALIGN, "qkv_mx_project: alignment (codes 16, exponents 4, w_packed 256, channel scale 16, bias 8, out 16, ssq 8, workspace 256)");
+  const int64_t Iq = (int64_t)num_heads * head_dim, Ik = (int64_t)num_kv_heads * head_dim;
+  return hip_status(launch_project_mx(a_codes, a_row_stride, a_e8m0, a_e8m0_stride,
+                                      (const uint8_t*)w_packed, w_channel_scale, bias, T, H, I,
+                                      Iq, Ik, head_dim, layout == QKVMX_LAYOUT_NBSD, out, ssq,
+                                      (uint8_t*)workspace, stream), "qkv_mx_project");
 }
 
 qkvmx_status qk_norm_rope_apply(uint16_t* qkv, const float* ssq, const uint16_t* q_gamma,

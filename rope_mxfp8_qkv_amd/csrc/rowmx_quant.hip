@@ -1,5 +1,7 @@
-// ROW_MX activation producers ([QKV-CTE] "Interface", packed_hidden: H FP8 codes + 4-byte fp32
-// scale tail per row; [RMSNORM-MX] residual / eps / unpadded_hidden_size).
+// Activation producers: ROW_MX rows ([QKV-CTE] "Interface", packed_hidden: H FP8 codes + 4-byte
+// fp32 scale tail per row) and MX block-32 rows ([RMSNORM-MX] qmx_output_dtype: E4M3 codes
+// with one E8M0 exponent per 32 elements; emit_norm_bf16), each optionally fused with the
+// residual add and RMSNorm ([RMSNORM-MX] residual / eps / unpadded_hidden_size).
 //
 // One block per row, two 8-element chunks per thread (H / 16 threads, rounded up to whole
 // wavefronts), the chunks of a thread one block-width apart so each wavefront load covers 1 KiB
@@ -110,16 +112,17 @@ __global__ void __launch_bounds__(1024) row_quantize_kernel(const void* __restri
   encode_store(y, amax, H, packed + row * (H + 4));
 }
 
+// Steps 1-4 of the fused producer for one row, into registers y (zeros past H):
+//   r = bf16_RNE(fp32(hid) + fp32(res)) -> res_out (r = hid without a residual);
+//   inv = fp32(1 / sqrt(sum r^2 / Hu + eps)), the sum (fixed order), sqrt and divide in fp64;
+//   y = fl32(fl32(r * inv) * gamma).
 template <bool RES>
-__global__ void __launch_bounds__(1024) rmsnorm_quantize_kernel(
-    const uint16_t* __restrict__ hid, const uint16_t* __restrict__ res,
-    const uint16_t* __restrict__ gamma, float eps, int64_t H, int64_t Hu,
-    uint16_t* __restrict__ res_out, uint8_t* __restrict__ packed) {
-  __shared__ double shd[kMaxWaves];
-  __shared__ float shf[kMaxWaves];
-  const int64_t row = blockIdx.x;
+__device__ __forceinline__ void normed_row(const uint16_t* __restrict__ hid,
+                                           const uint16_t* __restrict__ res,
+                                           const uint16_t* __restrict__ gamma, float eps,
+                                           int64_t H, int64_t Hu, uint16_t* __restrict__ res_out,
+                                           int64_t row, float (&y)[kCpt][kChunk], double* shd) {
   const int64_t nchunks = H / kChunk;
-  float y[kCpt][kChunk];
   double ss = 0.0;
 #pragma unroll
   for (int k = 0; k < kCpt; ++k) {
@@ -152,7 +155,6 @@ __global__ void __launch_bounds__(1024) rmsnorm_quantize_kernel(
   ss = block_sum(ss, shd);
   // inv = fp32(1 / sqrt(ss / Hu + eps)), sqrt and divide correctly rounded in fp64
   const float inv = (float)(1.0 / sqrt(ss / (double)Hu + (double)eps));
-  float amax = 0.0f;
 #pragma unroll
   for (int k = 0; k < kCpt; ++k) {
     const int64_t c = chunk_of(k);
@@ -160,14 +162,128 @@ __global__ void __launch_bounds__(1024) rmsnorm_quantize_kernel(
       float g[kChunk];
       unpack8(reinterpret_cast<const uint4*>(gamma)[c], g);
 #pragma unroll
-      for (int e = 0; e < kChunk; ++e) {
-        y[k][e] = (y[k][e] * inv) * g[e];    // two separately rounded fp32 products
-        amax = fmaxf(amax, fabsf(y[k][e]));
+      for (int e = 0; e < kChunk; ++e) y[k][e] = (y[k][e] * inv) * g[e];   // two fp32 roundings
+    }
+  }
+}
+
+template <bool RES>
+__global__ void __launch_bounds__(1024) rmsnorm_quantize_kernel(
+    const uint16_t* __restrict__ hid, const uint16_t* __restrict__ res,
+    const uint16_t* __restrict__ gamma, float eps, int64_t H, int64_t Hu,
+    uint16_t* __restrict__ res_out, uint8_t* __restrict__ packed) {
+  __shared__ double shd[kMaxWaves];
+  __shared__ float shf[kMaxWaves];
+  const int64_t row = blockIdx.x;
+  float y[kCpt][kChunk];
+  normed_row<RES>(hid, res, gamma, eps, H, Hu, res_out, row, y, shd);
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kCpt; ++k)
+#pragma unroll
+    for (int e = 0; e < kChunk; ++e) amax = fmaxf(amax, fabsf(y[k][e]));
+  amax = block_max(amax, shf);
+  encode_store(y, amax, H, packed + row * (H + 4));
+}
+
+// MX block-32 encoding of y (the 4 consecutive chunks of a 32-element block belong to 4
+// consecutive lanes, aligned to 4): block maximum by two lane exchanges, shared exponent
+// E = max(biased exponent of amax - 8, 0) (floor(log2 amax) - 8 + 127, clamped at 0; amax < 2^-119
+// or zero gives 0), codes = E4M3 RNE saturating of y * 2^(127 - E) (a power-of-two scaling,
+// exact for every value that does not round to zero); an all-zero block stores zero codes.
+// Codes go to codes_row (8 bytes per chunk), exponents through LDS to e8_row (dword stores).
+__device__ __forceinline__ void mx_encode_store(const float (&y)[kCpt][kChunk], int64_t H,
+                                                uint8_t* __restrict__ codes_row,
+                                                uint8_t* __restrict__ e8_row, uint8_t* sh_e) {
+  const int64_t nchunks = H / kChunk;
+#pragma unroll
+  for (int k = 0; k < kCpt; ++k) {
+    const int64_t c = chunk_of(k);
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kChunk; ++e) m = fmaxf(m, fabsf(y[k][e]));
+    // every lane of a 4-lane group takes part (a group is entirely inside or past the row)
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    const int eb = (int)((__float_as_uint(m) >> 23) & 0xFFu);
+    const uint32_t E = (uint32_t)max(eb - 8, 0);
+    const float inv = __uint_as_float((254u - E) << 23);          // 2^(127 - E)
+    if (c < nchunks) {
+      uint32_t lo = 0, hi = 0;
+      if (m > 0.0f) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lo |= f32_to_e4m3(y[k][e] * inv) << (8 * e);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hi |= f32_to_e4m3(y[k][4 + e] * inv) << (8 * e);
+      }
+      *reinterpret_cast<uint2*>(codes_row + c * kChunk) = make_uint2(lo, hi);
+      if ((c & 3) == 0) sh_e[c >> 2] = (uint8_t)E;
+    }
+  }
+  __syncthreads();
+  if (H % 128 == 0) {                              // whole dwords (the row start is 4-aligned)
+    for (int64_t i = threadIdx.x; i < H / 128; i += blockDim.x)
+      reinterpret_cast<uint32_t*>(e8_row)[i] = reinterpret_cast<const uint32_t*>(sh_e)[i];
+  } else {
+    for (int64_t i = threadIdx.x; i < H / 32; i += blockDim.x) e8_row[i] = sh_e[i];
+  }
+}
+
+// y = x (fp32 or bf16 rows), MX block-32 encoded.
+template <bool BF16>
+__global__ void __launch_bounds__(1024) mx_quantize_kernel(const void* __restrict__ x, int64_t H,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ e8) {
+  __shared__ __attribute__((aligned(4))) uint8_t sh_e[kMaxWaves * 64 * kCpt * kChunk / 32];
+  const int64_t row = blockIdx.x;
+  const int64_t nchunks = H / kChunk;
+  float y[kCpt][kChunk];
+#pragma unroll
+  for (int k = 0; k < kCpt; ++k) {
+    const int64_t c = chunk_of(k);
+#pragma unroll
+    for (int e = 0; e < kChunk; ++e) y[k][e] = 0.0f;
+    if (c < nchunks) {
+      if (BF16) {
+        unpack8(reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + row * H)[c],
+                y[k]);
+      } else {
+        const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) +
+                                                          row * H) + 2 * c;
+        const float4 a = p[0], b = p[1];
+        y[k][0] = a.x; y[k][1] = a.y; y[k][2] = a.z; y[k][3] = a.w;
+        y[k][4] = b.x; y[k][5] = b.y; y[k][6] = b.z; y[k][7] = b.w;
       }
     }
   }
-  amax = block_max(amax, shf);
-  encode_store(y, amax, H, packed + row * (H + 4));
+  mx_encode_store(y, H, codes + row * H, e8 + row * (H / 32), sh_e);
+}
+
+// Residual add + RMSNorm (the steps of rmsnorm_quantize_kernel), then MX block-32 encoding of
+// y and, with EMIT, y rounded to bf16 (RNE) into norm_out.
+template <bool RES, bool EMIT>
+__global__ void __launch_bounds__(1024) rmsnorm_mx_kernel(
+    const uint16_t* __restrict__ hid, const uint16_t* __restrict__ res,
+    const uint16_t* __restrict__ gamma, float eps, int64_t H, int64_t Hu,
+    uint16_t* __restrict__ res_out, uint8_t* __restrict__ codes, uint8_t* __restrict__ e8,
+    uint16_t* __restrict__ norm_out) {
+  __shared__ double shd[kMaxWaves];
+  __shared__ __attribute__((aligned(4))) uint8_t sh_e[kMaxWaves * 64 * kCpt * kChunk / 32];
+  const int64_t row = blockIdx.x;
+  float y[kCpt][kChunk];
+  normed_row<RES>(hid, res, gamma, eps, H, Hu, res_out, row, y, shd);
+  if (EMIT) {
+    const int64_t nchunks = H / kChunk;
+#pragma unroll
+    for (int k = 0; k < kCpt; ++k) {
+      const int64_t c = chunk_of(k);
+      if (c < nchunks)
+        reinterpret_cast<uint4*>(norm_out + row * H)[c] =
+            make_uint4(pack_bf16x2(y[k][0], y[k][1]), pack_bf16x2(y[k][2], y[k][3]),
+                       pack_bf16x2(y[k][4], y[k][5]), pack_bf16x2(y[k][6], y[k][7]));
+    }
+  }
+  mx_encode_store(y, H, codes + row * H, e8 + row * (H / 32), sh_e);
 }
 
 unsigned block_threads(int64_t H) {
@@ -196,6 +312,30 @@ hipError_t launch_rmsnorm_quantize(const uint16_t* hid, const uint16_t* res, con
   else
     hipLaunchKernelGGL(rmsnorm_quantize_kernel<false>, grid, block, 0, s, hid, res, gamma, eps,
                        H, Hu, res_out, packed);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quantize(const void* x, int dtype, int64_t T, int64_t H, uint8_t* codes,
+                              uint8_t* e8, hipStream_t s) {
+  const dim3 grid((unsigned)T), block(block_threads(H));
+  if (dtype == 1)
+    hipLaunchKernelGGL(mx_quantize_kernel<true>, grid, block, 0, s, x, H, codes, e8);
+  else
+    hipLaunchKernelGGL(mx_quantize_kernel<false>, grid, block, 0, s, x, H, codes, e8);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_mx(const uint16_t* hid, const uint16_t* res, const uint16_t* gamma,
+                             float eps, int64_t T, int64_t H, int64_t Hu, uint16_t* res_out,
+                             uint8_t* codes, uint8_t* e8, uint16_t* norm_out, hipStream_t s) {
+  const dim3 grid((unsigned)T), block(block_threads(H));
+  const int v = (res ? 2 : 0) | (norm_out ? 1 : 0);
+  switch (v) {
+    case 0: hipLaunchKernelGGL((rmsnorm_mx_kernel<false, false>), grid, block, 0, s, hid, res, gamma, eps, H, Hu, res_out, codes, e8, norm_out); break;
+    case 1: hipLaunchKernelGGL((rmsnorm_mx_kernel<false, true>), grid, block, 0, s, hid, res, gamma, eps, H, Hu, res_out, codes, e8, norm_out); break;
+    case 2: hipLaunchKernelGGL((rmsnorm_mx_kernel<true, false>), grid, block, 0, s, hid, res, gamma, eps, H, Hu, res_out, codes, e8, norm_out); break;
+    default: hipLaunchKernelGGL((rmsnorm_mx_kernel<true, true>), grid, block, 0, s, hid, res, gamma, eps, H, Hu, res_out, codes, e8, norm_out); break;
+  }
   return hipGetLastError();
 }
 

@@ -135,3 +135,39 @@ def test_producer_and_weight_validation():
     assert L.mx_weight_quantize(P, 100, 16, P, P, None) == 2
     assert L.qkv_weight_prepack(P, P, 256, 16, P, 10, None) == 2                 # buffer too small
     assert L.qkv_weight_prepack(P, P, 256, 16, P + 64, 1 << 20, None) == 3
+
+
+def _mxproj(L, **kw):
+    a = dict(a_codes=P, a_row_stride=256, a_e8m0=P, a_e8m0_stride=8, w_packed=P,
+             w_channel_scale=None, bias=None, T=4, H=256, num_heads=2, num_kv_heads=2,
+             head_dim=64, layout=0, out=P, ssq=None, workspace=P, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return L.qkv_mx_project(*a.values())
+
+
+def test_mx_path_validation():
+    from rope_mxfp8_qkv_amd import _abi
+    L = _lib()
+    # workspace: the sum-of-squares partials (one per 128 output channels: 120 at I = 15360)
+    # and the counter block; no activation stage images
+    assert L.qkv_mx_workspace_bytes(75600, 5120, 15360) == 120 * 75600 * 8 + 256
+    assert L.qkv_mx_workspace_bytes(4, 100, 16) == 0
+    assert _mxproj(L, a_e8m0=None) == 1
+    assert _mxproj(L, H=96, a_row_stride=96, a_e8m0_stride=4) == 6     # H % 256 != 0
+    assert "256" in _abi.last_error()
+    assert _mxproj(L, a_row_stride=264) == 2                           # not a multiple of 16
+    assert _mxproj(L, a_e8m0_stride=6) == 2                            # not a multiple of 4
+    assert _mxproj(L, a_e8m0_stride=4) == 2                            # < H / 32
+    assert _mxproj(L, a_codes=P + 4) == 3                              # codes 16-byte aligned
+    assert _mxproj(L, a_e8m0=P + 2) == 3
+    assert _mxproj(L, workspace=None) == 5
+    assert _mxproj(L, ssq=P, ws_bytes=8) == 5
+    assert _mxproj(L, layout=3) == 4
+    assert L.mx_block_quantize(P, 0, 4, 100, P, P, None) == 2
+    assert L.mx_block_quantize(P, 2, 4, 256, P, P, None) == 4
+    assert L.mx_block_quantize(P, 0, 4, 256, P + 4, P, None) == 3
+    assert L.mx_block_quantize(P, 0, 4, 32768, P, P, None) == 6
+    assert L.rmsnorm_mx_block_quantize(P, P, P, 1e-6, 4, 256, 0, None, P, P, None, None) == 4
+    assert L.rmsnorm_mx_block_quantize(P, None, P, 1e-6, 4, 256, 0, None, P, P, P + 8, None) == 3
+    assert L.rmsnorm_mx_block_quantize(P, None, P, -1.0, 4, 256, 0, None, P, P, None, None) == 4
+    assert L.rmsnorm_mx_block_quantize(None, None, P, 1e-6, 4, 256, 0, None, P, P, None, None) == 1
