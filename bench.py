@@ -11,7 +11,8 @@ Prints ONE JSON line.  ``value`` is the projection's algorithmic TFLOP/s over th
 the library launches on, averaged over the timed steps.  ``cpu_baseline`` times the CPU oracle
 (NumPy, fp64) on a bounded row sample of the same workload on this host.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5|3|2] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5|3|2] [--act rowmx|mx]
+                    [--layout bsd|nbsd] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -129,6 +130,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layout", choices=["bsd", "nbsd"], default="bsd",
                     help="output layout of the projection and pass 2 (BSD [T, I] or NBSd [I/d, T, d])")
+    ap.add_argument("--act", choices=["rowmx", "mx"], default="rowmx",
+                    help="activation encoding: ROW_MX rows with an fp32 row scale (the projection's "
+                         "packed_hidden) or MX block-32 (E8M0 exponent per 32 elements)")
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
@@ -171,11 +175,14 @@ def gen_inputs(cid, dev):
     return inp
 
 
-def algorithmic_bytes(p, producer: bool):
+def algorithmic_bytes(p, producer: bool, mx: bool = False):
     """Per-kernel algorithmic HBM bytes (each input read once, each output written once)."""
     T, H, Iq, Ik, d = p.T, p.H, p.Iq, p.Ik, p.head_dim
     nr = 4 * T * (Iq + Ik) + (8 * T * d if p.rope else 0) + 8 * T + 2 * (Iq + Ik)
-    prod = 4 * T * H + 2 * T * H + T * (H + 4) + 2 * H if producer else 0
+    # producer: hidden + residual in, residual sum out, encoded rows out (ROW_MX: H codes + fp32
+    # scale; MX: H codes + H / 32 exponents), gamma once
+    enc = T * (H + H // 32) if mx else T * (H + 4)
+    prod = 4 * T * H + 2 * T * H + enc + 2 * H if producer else 0
     return {"norm_rope": nr, "producer": prod}
 
 
@@ -202,28 +209,46 @@ def run_gpu(args):
     wp = q.prepare_weight(codes, e8, H, I)
     del inp["w"], codes, e8
 
-    packed = torch.empty((T, H + 4), dtype=torch.uint8, device=dev)
+    mx = args.act == "mx"
+    if mx:
+        codes_a = torch.empty((T, H), dtype=torch.uint8, device=dev)
+        e8_a = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+    else:
+        packed = torch.empty((T, H + 4), dtype=torch.uint8, device=dev)
     res_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if inp["producer"] else None
     layout = q.LAYOUT_NBSD if args.layout == "nbsd" else q.LAYOUT_BSD
     out = (torch.empty((I // p.head_dim, T, p.head_dim), dtype=torch.bfloat16, device=dev)
            if args.layout == "nbsd" else torch.empty((T, I), dtype=torch.bfloat16, device=dev))
     ssq = torch.empty((T, 2), dtype=torch.float32, device=dev)
-    ws = torch.empty(q.qkvmx_workspace_bytes(T, H, I), dtype=torch.uint8, device=dev)
+    ws_n = q.qkv_mx_workspace_bytes(T, H, I) if mx else q.qkvmx_workspace_bytes(T, H, I)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
     flags = q.NORM_Q | q.NORM_K | q.FUSED_ROPE
-    if not inp["producer"]:
-        q.row_quantize_packed(inp["x"], packed)     # activations fixed for the whole run
+    if not inp["producer"]:                         # activations fixed for the whole run
+        if mx:
+            q.mx_block_quantize(inp["x"], codes_a, e8_a)
+        else:
+            q.row_quantize_packed(inp["x"], packed)
 
     def step(ev=None):
         if ev:
             ev[0].record(stream)
         if inp["producer"]:
-            q.rmsnorm_mx_quantize(inp["hid"], inp["pgamma"], 1e-6, packed, residual=inp["res"],
-                                  residual_out=res_out)
+            if mx:
+                q.rmsnorm_mx_block_quantize(inp["hid"], inp["pgamma"], 1e-6, codes_a, e8_a,
+                                            residual=inp["res"], residual_out=res_out)
+            else:
+                q.rmsnorm_mx_quantize(inp["hid"], inp["pgamma"], 1e-6, packed,
+                                      residual=inp["res"], residual_out=res_out)
         if ev:
             ev[1].record(stream)
-        q.qkv_rowmx_project(packed, wp, out, H=H, num_heads=p.num_heads,
-                            num_kv_heads=p.num_kv_heads, head_dim=p.head_dim, bias=inp["bias"],
-                            ssq=ssq, workspace=ws, layout=layout)
+        if mx:
+            q.qkv_mx_project(codes_a, e8_a, wp, out, H=H, num_heads=p.num_heads,
+                             num_kv_heads=p.num_kv_heads, head_dim=p.head_dim, bias=inp["bias"],
+                             ssq=ssq, workspace=ws, layout=layout)
+        else:
+            q.qkv_rowmx_project(packed, wp, out, H=H, num_heads=p.num_heads,
+                                num_kv_heads=p.num_kv_heads, head_dim=p.head_dim,
+                                bias=inp["bias"], ssq=ssq, workspace=ws, layout=layout)
         if ev:
             ev[2].record(stream)
         q.qk_norm_rope_apply(out, num_heads=p.num_heads, num_kv_heads=p.num_kv_heads,
@@ -249,7 +274,7 @@ def run_gpu(args):
     ms = stage.mean(axis=0)          # producer, projection (+ sum reduce), norm/rope
     ms_step = wall * 1e3 / args.steps
     flops = 2.0 * T * H * I
-    nbytes = algorithmic_bytes(p, inp["producer"])
+    nbytes = algorithmic_bytes(p, inp["producer"], mx)
     proj_tflops = flops / (ms[1] * 1e-3) / 1e12
     res = {
         "ms_per_step": ms_step,
@@ -264,6 +289,7 @@ def run_gpu(args):
         "gen_s": inp["gen_s"],
         "p": p,
         "producer": inp["producer"],
+        "mx": mx,
     }
     return res
 
@@ -342,20 +368,23 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": ("producer + QKV projection + across-heads norm + 3-axis RoPE"
-                         if r["producer"] else "QKV projection + across-heads norm + RoPE"),
+                         if r["producer"] else "QKV projection + across-heads norm + RoPE")
+                        + (", MX block-32 activations" if r["mx"] else ", ROW_MX activations"),
             "T": p.T, "H": p.H, "I": p.I, "num_heads": p.num_heads,
             "num_kv_heads": p.num_kv_heads, "head_dim": p.head_dim,
             "grid": list(p.grid) if p.grid else None, "layout": args.layout.upper().replace("NBSD", "NBSd"),
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "qkv_rowmx_project (activation repack + project_kernel + ssq_reduce)",
+            "kernel": ("qkv_mx_project (project_kernel + ssq_reduce)" if r["mx"] else
+                       "qkv_rowmx_project (activation repack + project_kernel + ssq_reduce)"),
             "bound": "mfma",
             "achieved": ach,
             "peak": PEAK_MXFP8_TFLOPS,
             "unit": "TFLOP/s",
             "frac": ach / PEAK_MXFP8_TFLOPS,
-            "traffic": measured_traffic() if args.config == 5 and args.layout == "bsd" else None,
+            "traffic": (measured_traffic() if args.config == 5 and args.layout == "bsd"
+                        and not r["mx"] else None),
         },
         "stages": {
             "ms": r["stage_ms"],

@@ -180,8 +180,9 @@ qkvmx_status qkv_rowmx_project(const uint8_t* a_codes, int64_t a_row_stride,
                                uint16_t* out, float* ssq, void* workspace, size_t ws_bytes,
                                hipStream_t stream);
 
-/* Workspace bytes qkv_mx_project needs (the per-tile sums of squares and the tile counters;
- * the activation stages are read straight from the rows).  0 for invalid sizes. */
+/* Workspace bytes qkv_mx_project needs for a [T, H] x [H, I] call: the activation codes and
+ * their exponents re-laid in the kernel's LDS stage images (about T * H * 33 / 32 bytes) plus
+ * per-tile sums of squares.  0 for invalid sizes. */
 size_t qkv_mx_workspace_bytes(int64_t T, int64_t H, int64_t I);
 
 /* Pass 1 on MX block-32 activations ([RMSNORM-MX] qmx_output_dtype feeding [QKV-CTE]'s
@@ -191,10 +192,10 @@ size_t qkv_mx_workspace_bytes(int64_t T, int64_t H, int64_t I);
  * and ssq as there (fp32 values before rounding; V excluded).
  *   a_codes   E4M3 codes of row t at a_codes + t * a_row_stride (H bytes).
  *   a_e8m0    E8M0 exponents of row t at a_e8m0 + t * a_e8m0_stride (H / 32 bytes).
- *   workspace >= qkv_mx_workspace_bytes(T, H, I) bytes, 256-byte aligned, required; scratch.
- * Other arguments, layouts and errors as qkv_rowmx_project.  Requires H % 256 == 0
- * (QKVMX_ERR_UNSUPPORTED otherwise), a_row_stride >= H and a multiple of 16, a_codes 16-byte
- * aligned, a_e8m0_stride >= H / 32 and a multiple of 4, a_e8m0 4-byte aligned. */
+ *   workspace >= qkv_mx_workspace_bytes(T, H, I) bytes, 256-byte aligned, required; its
+ *             contents are scratch, as for qkv_rowmx_project.
+ * Other arguments, layouts and errors as qkv_rowmx_project.  Requires a_row_stride >= H and a
+ * multiple of 4, a_codes 4-byte aligned, a_e8m0_stride >= H / 32. */
 qkvmx_status qkv_mx_project(const uint8_t* a_codes, int64_t a_row_stride, const uint8_t* a_e8m0,
                             int64_t a_e8m0_stride, const void* w_packed,
                             const float* w_channel_scale, const uint16_t* bias, int64_t T,

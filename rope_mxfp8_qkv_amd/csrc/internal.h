@@ -65,13 +65,21 @@ inline size_t counters_offset(int64_t T, int64_t H, int64_t I) {
 inline size_t workspace_total_bytes(int64_t T, int64_t H, int64_t I) {
   return counters_offset(T, H, I) + kCounterBytes;
 }
-// MX-activation projection workspace (the activation stages are read from the rows): the
-// sum-of-squares partials [P][T][2] fp32, then the 256-byte counter block.
-inline size_t mx_counters_offset(int64_t T, int64_t I) {
-  return (partials_bytes(T, I) + 255) / 256 * 256;
+// MX-activation projection workspace: the activation code stage images (as above), their
+// exponents re-laid per (token tile, superstep) as [256][2] dwords, the sum-of-squares
+// partials, then the 256-byte counter block.
+inline size_t mx_scale_image_offset(int64_t T, int64_t H) { return act_image_bytes(T, H); }
+inline size_t mx_scale_image_bytes(int64_t T, int64_t H) {
+  return (size_t)ceil_div(T, kTileM) * (packed_stages(H) / 4) * kTileM * 2 * 4;
 }
-inline size_t mx_workspace_total_bytes(int64_t T, int64_t I) {
-  return mx_counters_offset(T, I) + kCounterBytes;
+inline size_t mx_partials_offset(int64_t T, int64_t H) {
+  return mx_scale_image_offset(T, H) + mx_scale_image_bytes(T, H);
+}
+inline size_t mx_counters_offset(int64_t T, int64_t H, int64_t I) {
+  return (mx_partials_offset(T, H) + partials_bytes(T, I) + 255) / 256 * 256;
+}
+inline size_t mx_workspace_total_bytes(int64_t T, int64_t H, int64_t I) {
+  return mx_counters_offset(T, H, I) + kCounterBytes;
 }
 
 hipError_t launch_mx_weight_quantize(const float* w, int64_t H, int64_t I, uint8_t* codes,

@@ -72,8 +72,8 @@ struct ProjectArgs {
   const uint8_t* w_img;        // [NT][KS][16 KiB]
   const uint8_t* w_scales;     // [KS / 4][NT * 256][2] dwords
   const uint8_t* x_img;        // activation stage images [MT][KS][16 KiB] (workspace; ROW_MX)
-  const uint8_t* x_e8;         // MX block-32 activations: E8M0 exponents, row t at t * e_stride
-  int64_t e_stride;
+  const uint8_t* x_scales;     // MX block-32 activations: exponent images [MT][KS / 4][256][2]
+                               // dwords (workspace), the weight exponents' format
   const float* chan_scale;     // [I] or null
   const uint16_t* bias;        // [I] or null
   int64_t T, H, I, Iq, Ik;
@@ -114,15 +114,6 @@ __device__ __forceinline__ void dma16_blk(uint32_t base, const uint8_t* sbase, u
     default: QKVMX_DMA_BLK(3072); break;
   }
 #undef QKVMX_DMA_BLK
-}
-// 1 KiB block I of a stage straight from activation rows: lane L reads sbase + voff_L (a row
-// chunk of its own) and writes LDS at the stage buffer + 1024 I + 16 L; the LDS offset rides in
-// M0, the global address carries no immediate.
-template <int Q, int I>
-__device__ __forceinline__ void dma16_row(uint32_t base, const uint8_t* sbase, uint32_t voff) {
-  asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(base), "v"(voff), "s"(sbase), "n"(Q * kStageImage + 1024 * I)
-               : "memory", "m0", "scc");
 }
 // Dword DMA from a per-lane 64-bit address (lane L: 4 bytes from g_L to LDS lds + 4 L).
 __device__ __forceinline__ void dma4g(uint32_t lds, const void* g) {
@@ -170,16 +161,15 @@ __device__ __forceinline__ Tile decode_tile(int tile, int tiles_m, int tiles_n) 
   return Tile{first_m + in_group % gm, in_group / gm};
 }
 
-// kMx: MX block-32 activations (E4M3 rows with one E8M0 exponent per 32 elements).  The rows
-// are 16-byte aligned, so the activation stages are DMA-copied straight from them (no per-call
-// stage images); their exponents feed the MFMA's B-scale as the weight's feed the A-scale, and
-// the epilogue has no row scale.
+// kMx: MX block-32 activations (E4M3 rows with one E8M0 exponent per 32 elements).  Their
+// exponents, re-laid per call in the weight exponents' format, feed the MFMA's B-scale as the
+// weight's feed the A-scale, and the epilogue has no row scale.
 template <bool kChanScale, bool kBias, bool kNbsd, bool kMx>
 __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_w[kBufs][kStageImage];
   __shared__ __attribute__((aligned(16))) uint8_t lds_x[kBufs][kStageImage];
   __shared__ __attribute__((aligned(16))) uint8_t lds_sc[2][kTileN * 8];
-  // MX: activation exponents of a superstep, [token][8 bytes] in row order (2 ring slots)
+  // MX: activation exponents of a superstep (2 ring slots, the layout of lds_sc)
   __shared__ __attribute__((aligned(16))) uint8_t lds_xsc[kMx ? 2 : 1][kMx ? kTileM * 8 : 16];
   // epilogue operands, double-buffered (the next tile's arrive while the current tile's are
   // in use): channel scale and row scale (fp32) and the bias, DMA-copied as raw bf16 pairs and
@@ -228,63 +218,25 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   // ---- DMA sources of the current tile (wave-uniform bases, in SGPRs) ----
   // weight: wave w copies 1 KiB blocks 4 w .. 4 w + 3 of each 16 KiB stage image;
   // exponents: each wave copies 512 bytes (two dword DMAs) of the 2 KiB per superstep;
-  // activation: same scheme as the weight, from the per-call stage images (ROW_MX), or
-  // straight from the rows (MX: lane L of block i copies its own 16-byte chunk, the logical
-  // chunk (L % 4) ^ stage_swizzle(row) of row 64 w + 16 i + L / 4, rows past T clamped to the
-  // last one; xv[i] is that chunk's byte offset in the codes, xsv[j] the offset of exponent
-  // dword 128 w + 64 j + L of the tile's [256 tokens][8 bytes] per superstep)
+  // activation: same scheme as the weight, from the per-call stage images; MX exponents: as
+  // the weight's, from their per-call images
   const uint32_t wdst = lds_addr(&lds_w[0][0]) + wave * 4096;
   const uint32_t xdst = lds_addr(&lds_x[0][0]) + wave * 4096;
   const uint32_t sdst = lds_addr(&lds_sc[0][0]) + wave * 512;
   const uint32_t xsdst = lds_addr(&lds_xsc[0][0]) + wave * 512;
   const int64_t s_step = (int64_t)a.tiles_n * kTileN * 2 * 4;       // bytes per superstep
+  const int64_t xs_step = (int64_t)kTileM * 2 * 4;                  // MX: per superstep
   const uint8_t* wbase;
   const uint8_t* xbase;
   const uint8_t* sbase;
-  uint32_t xv[4] = {0u, 0u, 0u, 0u}, xsv[2] = {0u, 0u};
+  const uint8_t* xsbase;
   auto set_sources = [&](Tile u) {
     wbase = a.w_img + ((int64_t)u.tn * a.KS) * kStageImage + wave * 4096;
     sbase = a.w_scales + ((int64_t)u.tn * kTileN * 2) * 4 + wave * 512;
-    if (kMx) {
-      xbase = a.a_codes;
-      const int lv = fresh_lane();
-      const int64_t m0 = (int64_t)u.tm * kTileM;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wave * 64 + 16 * i + (lv >> 2);
-        const int c = (lv & 3) ^ stage_swizzle(row);
-        xv[i] = (uint32_t)(min(m0 + row, a.T - 1) * a.a_stride + 16 * c);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int d = wave * 128 + 64 * j + lv;
-        xsv[j] = (uint32_t)(min(m0 + (d >> 1), a.T - 1) * a.e_stride + 4 * (d & 1));
-      }
-    } else {
-      xbase = a.x_img + ((int64_t)u.tm * a.KS) * kStageImage + wave * 4096;
-    }
+    xbase = a.x_img + ((int64_t)u.tm * a.KS) * kStageImage + wave * 4096;
+    if (kMx) xsbase = a.x_scales + (int64_t)u.tm * (a.KS / 4) * xs_step + wave * 512;
   };
   set_sources(t);
-
-  // activation DMA of 1 KiB block i of stage t (Q = t % 4)
-  auto xdma = [&](auto q_c, int t, uint32_t voff16, int i) __attribute__((always_inline)) {
-    constexpr int Q = decltype(q_c)::value;
-    if (kMx) {
-      const uint8_t* const src = xbase + (int64_t)t * kStage;
-      switch (i) {
-        case 0: dma16_row<Q, 0>(xdst, src, xv[0]); break;
-        case 1: dma16_row<Q, 1>(xdst, src, xv[1]); break;
-        case 2: dma16_row<Q, 2>(xdst, src, xv[2]); break;
-        default: dma16_row<Q, 3>(xdst, src, xv[3]); break;
-      }
-    } else {
-      dma16_blk<Q>(xdst, xbase + (int64_t)t * kStageImage, voff16, i);
-    }
-  };
-  // MX: exponent dword j of superstep sup into ring slot sup % 2
-  auto xsdma = [&](int64_t sup, int j) __attribute__((always_inline)) {
-    dma4(xsdst + (uint32_t)(sup & 1) * 2048 + 256 * j, a.x_e8 + sup * 8, xsv[j]);
-  };
 
   // DMA of stage t (t % 4 == Q) into buffer Q; a stage opening a superstep also brings that
   // superstep's exponents into ring slot (t / 4) % 2.
@@ -298,15 +250,17 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
       dma4(slot, sbase + sup * s_step, voff4);
       dma4(slot + 256, sbase + sup * s_step + 256, voff4);
       if (kMx) {
-        xsdma(sup, 0);
-        xsdma(sup, 1);
+        const uint32_t xslot = xsdst + (uint32_t)(sup & 1) * 2048;
+        dma4(xslot, xsbase + sup * xs_step, voff4);
+        dma4(xslot + 256, xsbase + sup * xs_step + 256, voff4);
       }
     }
     const uint8_t* const wsrc_t = wbase + (int64_t)t * kStageImage;
+    const uint8_t* const xsrc_t = xbase + (int64_t)t * kStageImage;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       dma16_blk<Q>(wdst, wsrc_t, voff16, i);
-      xdma(q_c, t, voff16, i);
+      dma16_blk<Q>(xdst, xsrc_t, voff16, i);
     }
   };
 
@@ -346,7 +300,7 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   // lane-derived LDS offsets of the K-steps, recomputed at the start of every tile (from a
   // fresh lane index) so that none of them is live across the epilogue
   int rw0, rw1, rx0, rx1, rsc, rxs;
-  uint32_t kvoff16, xsel;
+  uint32_t kvoff16;
   auto set_lane_offsets = [&]() {
     const int lv = fresh_lane();
     const int g = lv >> 5;
@@ -358,10 +312,7 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     rw0 = lds_off(w_row0, g); rw1 = lds_off(w_row0, 2 + g);
     rx0 = lds_off(x_row0, g); rx1 = lds_off(x_row0, 2 + g);
     rsc = (w_row0 * 2 + g) * 4;         // + 32 * 8 cf: this lane's exponent dword
-    // MX: this lane's token's 8 exponent bytes (+ 32 * 8 tf); byte q of the B-scale operand of
-    // K-step q must be the exponent of K-block 2 q + g of the superstep
-    rxs = x_row0 * 8;
-    xsel = 0x06040200u + 0x01010101u * (uint32_t)g;
+    rxs = (x_row0 * 2 + g) * 4;         // + 32 * 8 tf: MX, this lane's activation exponents
     kvoff16 = lv * 16;
   };
 
@@ -389,10 +340,8 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   auto xsload = [&](int slot, uint32_t (&xd)[4]) {
     if (kMx) {
 #pragma unroll
-      for (int tf = 0; tf < 4; ++tf) {
-        const uint2 v = *reinterpret_cast<const uint2*>(&lds_xsc[slot][rxs + 256 * tf]);
-        xd[tf] = __builtin_amdgcn_perm(v.y, v.x, xsel);
-      }
+      for (int tf = 0; tf < 4; ++tf)
+        xd[tf] = *reinterpret_cast<const uint32_t*>(&lds_xsc[slot][rxs + 256 * tf]);
     }
   };
 
@@ -420,6 +369,7 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     constexpr int nb = (q + 1) & (kBufs - 1);      // buffer of stage s + 1 (s % 4 == q)
     const int t = s + 4;                           // stage requested by this step
     const uint8_t* const wsrc_t = wbase + (int64_t)t * kStageImage;
+    const uint8_t* const xsrc_t = xbase + (int64_t)t * kStageImage;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int cf = k >> 2, tf = k & 3;
@@ -443,13 +393,15 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
           if ((k & 1) == 0)
             dma16_blk<q>(wdst, wsrc_t, kvoff16, i);
           else
-            xdma(q_c, t, kvoff16, i);
+            dma16_blk<q>(xdst, xsrc_t, kvoff16, i);
         } else if (q == 0 && (k == 8 || k == 9)) {
           const int64_t sup = t >> 2;
           const uint32_t slot = sdst + (uint32_t)(sup & 1) * 2048;
           dma4(slot + (k - 8) * 256, sbase + sup * s_step + (k - 8) * 256, kvoff16 >> 2);
         } else if (kMx && q == 0 && (k == 10 || k == 11)) {
-          xsdma(t >> 2, k - 10);
+          const int64_t sup = t >> 2;
+          const uint32_t xslot = xsdst + (uint32_t)(sup & 1) * 2048;
+          dma4(xslot + (k - 10) * 256, xsbase + sup * xs_step + (k - 10) * 256, kvoff16 >> 2);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -740,9 +692,25 @@ __global__ void __launch_bounds__(256) act_repack_kernel(const uint8_t* __restri
   reinterpret_cast<uint4*>(img)[(tm * KS + t) * (kStageImage / 16) + p] = o;
 }
 
-// Clears the per-XCD tile counters (the MX path has no repack kernel to do it).
-__global__ void counters_reset_kernel(unsigned* __restrict__ ctr) {
-  if (threadIdx.x < kXcds) ctr[threadIdx.x] = 0;
+// MX activation exponents [T, stride] -> per (token tile tm, superstep s) [256 tokens][2]
+// dwords: byte q of dword g of token r = exponent of K-block 8 s + 2 q + g of row 256 tm + r,
+// 127 (2^0) past T or H (whose codes are zero).  One thread per (token, dword).
+__global__ void __launch_bounds__(256) act_scale_repack_kernel(const uint8_t* __restrict__ e8,
+                                                               int64_t stride, int64_t T,
+                                                               int64_t H, uint32_t* __restrict__ img) {
+  const int64_t s = blockIdx.y, tm = blockIdx.z;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;       // 0 .. 511
+  const int r = idx >> 1, g = idx & 1;
+  const int64_t m = tm * kTileM + r;
+  const int64_t nblocks = H / 32;
+  uint32_t w = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t b = 8 * s + 2 * q + g;
+    const uint32_t e = (m < T && b < nblocks) ? e8[m * stride + b] : 127u;
+    w |= e << (8 * q);
+  }
+  img[((tm * gridDim.y + s) * kTileM + r) * 2 + g] = w;
 }
 
 // ssq[t] = sum over partials p < P of ws[p][t]; P = 0 gives zeros.  A block covers 64 tokens
@@ -858,10 +826,19 @@ hipError_t launch_project_mx(const uint8_t* a_codes, int64_t a_stride, const uin
                              uint8_t* ws, hipStream_t s) {
   ProjectArgs a = common_args(w_packed, chan_scale, bias, T, H, I, Iq, Ik, d, out);
   a.a_codes = a_codes; a.a_stride = a_stride;
-  a.x_e8 = a_e8; a.e_stride = e_stride;
-  a.ws = ssq ? reinterpret_cast<float*>(ws) : nullptr;
-  a.ctr = reinterpret_cast<unsigned*>(ws + mx_counters_offset(T, I));
-  hipLaunchKernelGGL(counters_reset_kernel, dim3(1), dim3(64), 0, s, a.ctr);
+  a.x_img = ws;
+  a.x_scales = ws + mx_scale_image_offset(T, H);
+  float* partials = reinterpret_cast<float*>(ws + mx_partials_offset(T, H));
+  a.ws = ssq ? partials : nullptr;
+  a.ctr = reinterpret_cast<unsigned*>(ws + mx_counters_offset(T, H, I));
+  // the activation codes re-laid as stage images (this kernel also resets the tile counters),
+  // their exponents in the weight exponents' format
+  dim3 rg(kStageImage / 16 / 256, (unsigned)a.KS, (unsigned)a.tiles_m);
+  hipLaunchKernelGGL(act_repack_kernel, rg, dim3(256), 0, s, a_codes, a_stride, T, H, a.KS, ws,
+                     a.ctr);
+  dim3 sg(2, (unsigned)(a.KS / 4), (unsigned)a.tiles_m);
+  hipLaunchKernelGGL(act_scale_repack_kernel, sg, dim3(256), 0, s, a_e8, e_stride, T, H,
+                     reinterpret_cast<uint32_t*>(ws + mx_scale_image_offset(T, H)));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_core<true>(a, chan_scale, bias, nbsd, ssq, s);

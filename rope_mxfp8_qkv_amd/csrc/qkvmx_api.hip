@@ -185,7 +185,7 @@ qkvmx_status qkv_rowmx_project(const uint8_t* a_codes, int64_t a_row_stride,
 
 size_t qkv_mx_workspace_bytes(int64_t T, int64_t H, int64_t I) {
   if (T <= 0 || H <= 0 || I <= 0 || H % 32) return 0;
-  return mx_workspace_total_bytes(T, I);
+  return mx_workspace_total_bytes(T, H, I);
 }
 
 qkvmx_status qkv_mx_project(const uint8_t* a_codes, int64_t a_row_stride, const uint8_t* a_e8m0,
@@ -197,14 +197,12 @@ qkvmx_status qkv_mx_project(const uint8_t* a_codes, int64_t a_row_stride, const 
   if (!a_codes || !a_e8m0 || !w_packed || !out) return fail(QKVMX_ERR_NULL, "qkv_mx_project: null pointer");
   if (!workspace) return fail(QKVMX_ERR_WORKSPACE, "qkv_mx_project: workspace is required");
   if (T <= 0 || H <= 0 || H % 32) return fail(QKVMX_ERR_SHAPE, "qkv_mx_project: need T > 0, H %% 32 == 0");
-  if (H % 256)
-    return fail(QKVMX_ERR_UNSUPPORTED, "qkv_mx_project: needs H %% 256 == 0 (activation stages are read straight from the rows)");
   if (num_heads < 1 || num_kv_heads < 0 || head_dim <= 0 || head_dim % 16)
     return fail(QKVMX_ERR_SHAPE, "qkv_mx_project: need num_heads >= 1, num_kv_heads >= 0, head_dim %% 16 == 0");
   if (layout != QKVMX_LAYOUT_BSD && layout != QKVMX_LAYOUT_NBSD)
     return fail(QKVMX_ERR_ARG, "qkv_mx_project: layout must be QKVMX_LAYOUT_BSD or QKVMX_LAYOUT_NBSD");
-  if (a_row_stride < H || a_row_stride % 16 || a_e8m0_stride < H / 32 || a_e8m0_stride % 4)
-    return fail(QKVMX_ERR_SHAPE, "qkv_mx_project: a_row_stride >= H and a multiple of 16, a_e8m0_stride >= H / 32 and a multiple of 4");
+  if (a_row_stride < H || a_row_stride % 4 || a_e8m0_stride < H / 32)
+    return fail(QKVMX_ERR_SHAPE, "qkv_mx_project: a_row_stride >= H and a multiple of 4, a_e8m0_stride >= H / 32");
   const int64_t I = (int64_t)(num_heads + 2 * (int64_t)num_kv_heads) * head_dim;
   if ((T - 1) * a_row_stride + H >= kMaxOffset || (T - 1) * a_e8m0_stride + H / 32 >= kMaxOffset)
     return fail(QKVMX_ERR_UNSUPPORTED, "qkv_mx_project: activation spans must be < 2^31 bytes");
@@ -212,12 +210,12 @@ qkvmx_status qkv_mx_project(const uint8_t* a_codes, int64_t a_row_stride, const 
     return fail(QKVMX_ERR_UNSUPPORTED, "qkv_mx_project: I must be < 2^22");
   if (layout == QKVMX_LAYOUT_NBSD && 2 * ((256 + (int64_t)head_dim) * T + 257 * (int64_t)head_dim) >= kMaxOffset)
     return fail(QKVMX_ERR_UNSUPPORTED, "qkv_mx_project: NBSd needs 2 ((256 + head_dim) T + 257 head_dim) < 2^31");
-  if (ws_bytes < mx_workspace_total_bytes(T, I))
-    return fail(QKVMX_ERR_WORKSPACE, "qkv_mx_project: workspace %zu < %zu bytes", ws_bytes, mx_workspace_total_bytes(T, I));
-  if (!aligned(a_codes, 16) || !aligned(a_e8m0, 4) || !aligned(w_packed, 256) ||
+  if (ws_bytes < mx_workspace_total_bytes(T, H, I))
+    return fail(QKVMX_ERR_WORKSPACE, "qkv_mx_project: workspace %zu < %zu bytes", ws_bytes, mx_workspace_total_bytes(T, H, I));
+  if (!aligned(a_codes, 4) || !aligned(w_packed, 256) ||
       (w_channel_scale && !aligned(w_channel_scale, 16)) || (bias && !aligned(bias, 8)) ||
       !aligned(out, 16) || (ssq && !aligned(ssq, 8)) || !aligned(workspace, 256))
-    return fail(QKVMX_ERR_ALIGN, "qkv_mx_project: alignment (codes 16, exponents 4, w_packed 256, channel scale 16, bias 8, out 16, ssq 8, workspace 256)");
+    return fail(QKVMX_ERR_ALIGN, "qkv_mx_project: alignment (codes 4, w_packed 256, channel scale 16, bias 8, out 16, ssq 8, workspace 256)");
   const int64_t Iq = (int64_t)num_heads * head_dim, Ik = (int64_t)num_kv_heads * head_dim;
   return hip_status(launch_project_mx(a_codes, a_row_stride, a_e8m0, a_e8m0_stride,
                                       (const uint8_t*)w_packed, w_channel_scale, bias, T, H, I,

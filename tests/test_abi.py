@@ -148,21 +148,21 @@ def _mxproj(L, **kw):
 def test_mx_path_validation():
     from rope_mxfp8_qkv_amd import _abi
     L = _lib()
-    # workspace: the sum-of-squares partials (one per 128 output channels: 120 at I = 15360)
-    # and the counter block; no activation stage images
-    assert L.qkv_mx_workspace_bytes(75600, 5120, 15360) == 120 * 75600 * 8 + 256
+    # workspace: code stage images (296 token tiles x 80 stages x 16 KiB), exponent images
+    # (296 x 20 supersteps x 2 KiB), the sum-of-squares partials (one per 128 output channels:
+    # 120 at I = 15360), 256-byte alignment, the counter block
+    part_end = 296 * 80 * 16384 + 296 * 20 * 2048 + 120 * 75600 * 8
+    assert L.qkv_mx_workspace_bytes(75600, 5120, 15360) == (part_end + 255) // 256 * 256 + 256
     assert L.qkv_mx_workspace_bytes(4, 100, 16) == 0
     assert _mxproj(L, a_e8m0=None) == 1
-    assert _mxproj(L, H=96, a_row_stride=96, a_e8m0_stride=4) == 6     # H % 256 != 0
-    assert "256" in _abi.last_error()
-    assert _mxproj(L, a_row_stride=264) == 2                           # not a multiple of 16
-    assert _mxproj(L, a_e8m0_stride=6) == 2                            # not a multiple of 4
+    assert _mxproj(L, H=100, a_row_stride=100, a_e8m0_stride=4) == 2    # H % 32 != 0
+    assert _mxproj(L, a_row_stride=258) == 2                           # not a multiple of 4
     assert _mxproj(L, a_e8m0_stride=4) == 2                            # < H / 32
-    assert _mxproj(L, a_codes=P + 4) == 3                              # codes 16-byte aligned
-    assert _mxproj(L, a_e8m0=P + 2) == 3
+    assert _mxproj(L, a_codes=P + 2) == 3                              # codes 4-byte aligned
     assert _mxproj(L, workspace=None) == 5
     assert _mxproj(L, ssq=P, ws_bytes=8) == 5
     assert _mxproj(L, layout=3) == 4
+    assert "layout" in _abi.last_error()
     assert L.mx_block_quantize(P, 0, 4, 100, P, P, None) == 2
     assert L.mx_block_quantize(P, 2, 4, 256, P, P, None) == 4
     assert L.mx_block_quantize(P, 0, 4, 256, P + 4, P, None) == 3

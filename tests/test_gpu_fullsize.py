@@ -64,12 +64,19 @@ class Gpu:
         return fl
 
 
-def check_projection(p, packed_rows_ref, w_codes, w_e8, bias, gq, gk, out, ssq, rows, fl):
-    """Oracle on the sampled rows vs the GPU's pass-1 sums and final (pass-2) outputs."""
-    codes, sA = oracle.rowmx_unpack(packed_rows_ref, p.H)
+def check_projection(p, packed_rows_ref, w_codes, w_e8, bias, gq, gk, out, ssq, rows, fl,
+                     mx_rows_ref=None):
+    """Oracle on the sampled rows vs the GPU's pass-1 sums and final (pass-2) outputs.  The
+    activation rows are ROW_MX packed rows, or (mx_rows_ref) MX block-32 codes and exponents."""
     W = oracle.mx_weight_decode(w_codes, w_e8)
+    if mx_rows_ref is None:
+        codes, sA = oracle.rowmx_unpack(packed_rows_ref, p.H)
+        a_e8 = None
+    else:
+        (codes, a_e8), sA = mx_rows_ref, None
     X, ssq_ref = oracle.project(codes, sA, w_codes, w_e8, None, bias, num_heads=p.num_heads,
-                                num_kv_heads=p.num_kv_heads, head_dim=p.head_dim, w_dense=W)
+                                num_kv_heads=p.num_kv_heads, head_dim=p.head_dim, w_dense=W,
+                                a_e8m0=a_e8)
     cos, sin = synth.rope_tables(p, rows)
     if fl:
         ref = oracle.norm_rope(None, ssq_ref, gq, gk if fl & 2 else None, cos, sin,
@@ -137,6 +144,55 @@ def test_fullsize_self_attention_video():
 def test_fullsize_producer_then_self_attention():
     """bf16 hidden + residual -> fused producer -> projection -> norm + 3-axis RoPE."""
     _run_self_attention(synth.CONFIGS[5].calls[0], producer=True)
+
+
+def test_fullsize_mx_producer_then_self_attention():
+    """MX block-32 path at the full video shape: bf16 hidden + residual -> residual add +
+    RMSNorm + E4M3 codes with per-32 exponents (and the bf16 normed rows) -> projection with
+    per-block activation exponents -> norm + 3-axis RoPE."""
+    import torch
+    q = __import__("rope_mxfp8_qkv_amd")
+    q.lib()
+    dev = G.torch_dev()
+    gpu = Gpu(q, dev)
+    p = synth.CONFIGS[5].calls[0]
+    rows = sample_rows(p.T)
+    print(f"[fullsize] {p.name} (MX block-32): T={p.T} H={p.H} I={p.I} rows={len(rows)}", flush=True)
+    hid, res, gam = synth.producer_inputs(p.seed_id, p.T, p.H)
+    codes = torch.empty((p.T, p.H), dtype=torch.uint8, device=dev)
+    e8 = torch.empty((p.T, p.H // 32), dtype=torch.uint8, device=dev)
+    res_out = torch.empty((p.T, p.H), dtype=torch.bfloat16, device=dev)
+    norm = torch.empty((p.T, p.H), dtype=torch.bfloat16, device=dev)
+    q.rmsnorm_mx_block_quantize(G.bf16_dev(hid, dev), G.bf16_dev(gam, dev), 1e-6, codes, e8,
+                                residual=G.bf16_dev(res, dev), residual_out=res_out,
+                                norm_out=norm)
+    r_ref, c_ref, e_ref, n_ref, _ = oracle.rmsnorm_mx(hid[rows], res[rows], gam, 1e-6)
+    del hid, res
+    ti = _idx(rows, dev)
+    G.check_equal(G.bf16_host(res_out[ti]), r_ref, "residual_out rows")
+    G.check_equal(G.bf16_host(norm[ti]), n_ref, "bf16 norm rows")
+    G.check_equal(codes[ti].cpu().numpy(), c_ref, "MX code rows")
+    G.check_equal(e8[ti].cpu().numpy(), e_ref, "MX exponent rows")
+    del res_out, norm
+    w = synth.weight(p)
+    wcodes, we8, wp = gpu.weight(w)
+    w_codes, w_e8 = oracle.mx_weight_quantize(w)
+    G.check_equal(wcodes.cpu().numpy(), w_codes, "weight codes")
+    bias, gq, gk = synth.bias_bf16(p), synth.gamma_bf16(p, "q"), synth.gamma_bf16(p, "k")
+    cos, sin = synth.rope_tables(p)
+    out = torch.empty((p.T, p.I), dtype=torch.bfloat16, device=dev)
+    ssq = torch.empty((p.T, 2), dtype=torch.float32, device=dev)
+    ws = torch.empty(q.qkv_mx_workspace_bytes(p.T, p.H, p.I), dtype=torch.uint8, device=dev)
+    q.qkv_mx_project(codes, e8, wp, out, H=p.H, num_heads=p.num_heads,
+                     num_kv_heads=p.num_kv_heads, head_dim=p.head_dim,
+                     bias=G.bf16_dev(bias, dev), ssq=ssq, workspace=ws)
+    seg = (p.num_heads + p.num_kv_heads) * p.head_dim
+    v_before = out[ti, seg:].clone()
+    fl = gpu.pass2(p, out, ssq, gq, gk, cos, sin)
+    torch.cuda.synchronize()
+    assert torch.equal(out[ti, seg:].view(torch.int16), v_before.view(torch.int16))
+    check_projection(p, None, w_codes, w_e8, bias, gq, gk, out, ssq, rows, fl,
+                     mx_rows_ref=(c_ref, e_ref))
 
 
 def test_fullsize_cross_attention_separate_calls():

@@ -106,6 +106,8 @@ MX_CASES = [
     ("single-seg", G.custom_projection("mss", T=257, H=1024, nq=5, nkv=0, d=128, rope=None), "bsd", False),
     ("T1", G.custom_projection("mt1", T=1, H=256, nq=2, nkv=2, d=64), "bsd", False),
     ("nbsd-ragged", G.custom_projection("mnb", T=300, H=512, nq=3, nkv=1, d=48), "nbsd", True),
+    ("ragged-H", G.custom_projection("mrh", T=200, H=352, nq=2, nkv=2, d=64), "bsd", False),
+    ("H96", G.custom_projection("mh96", T=70, H=96, nq=1, nkv=1, d=64), "bsd", False),
 ]
 
 
@@ -147,17 +149,18 @@ def test_mx_projection_parity(name, p, layout, chan):
 
 
 def test_mx_projection_strided_rows():
-    """Row strides beyond H (codes padded to a 16-byte multiple, exponents to a dword)."""
+    """Row strides beyond H (codes padded by 52 bytes: rows only 4-byte aligned; exponents
+    padded by 3 bytes)."""
     import torch
     q = _lib()
     dev = G.torch_dev()
     p = G.custom_projection("mst", T=200, H=512, nq=2, nkv=1, d=128)
     x = _blocky_activation(p.T, p.H, 31)
     codes, e8 = oracle.mx_block_quantize(x)
-    cpad = np.zeros((p.T, p.H + 48), np.uint8)
+    cpad = np.zeros((p.T, p.H + 52), np.uint8)
     cpad[:, :p.H] = codes
     cpad[:, p.H:] = 0x7F                            # NaN codes outside the rows: never read
-    epad = np.full((p.T, p.H // 32 + 4), 0xFF, np.uint8)
+    epad = np.full((p.T, p.H // 32 + 3), 0xFF, np.uint8)
     epad[:, :p.H // 32] = e8
     w_codes, w_e8m0 = oracle.mx_weight_quantize(synth.weight(p))
     bias = synth.bias_bf16(p)
