@@ -20,6 +20,14 @@ constexpr int kChunk = 8;                  // elements per chunk (one 16-byte bf
 constexpr int kCpt = 2;                    // chunks per thread
 constexpr int kMaxWaves = 16;              // H <= 16384
 typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// 8 bf16 values read once (streaming load: the producer's inputs are not re-read).
+__device__ __forceinline__ uint4 ntload16(const uint16_t* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ float block_max(float v, float* sh) {
 #pragma unroll
@@ -59,9 +67,15 @@ __device__ __forceinline__ int64_t chunk_of(int k) { return threadIdx.x + (int64
 
 // s = fl32(amax / 448) (IEEE division); codes = E4M3 RNE saturating of fl32(y / s); a zero row
 // stores s = 0 and zero codes; thread 0 writes the scale tail.
+// fl32(y / s) is formed as fl32(fl64(y * fl64(1 / s))): the fp64 product is within 2^-52 of
+// y / s, while a quotient of two fp32 numbers never is an fp32 rounding midpoint and lies at
+// least 2^-49 (relative) away from every one, so rounding the product to fp32 gives exactly the
+// IEEE quotient for every normal result (results below 2^-126 encode to a signed zero code
+// either way).  One fp64 divide per thread replaces an fp32 divide per element.
 __device__ __forceinline__ void encode_store(const float (&y)[kCpt][kChunk], float amax,
                                              int64_t H, uint8_t* __restrict__ row_out) {
   const float s = amax / 448.0f;
+  const double rinv = 1.0 / (double)s;
   const int64_t nchunks = H / kChunk;
 #pragma unroll
   for (int k = 0; k < kCpt; ++k) {
@@ -70,9 +84,10 @@ __device__ __forceinline__ void encode_store(const float (&y)[kCpt][kChunk], flo
       uint32_t lo = 0, hi = 0;
       if (s > 0.0f) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lo |= f32_to_e4m3(y[k][e] / s) << (8 * e);
+        for (int e = 0; e < 4; ++e) lo |= f32_to_e4m3((float)((double)y[k][e] * rinv)) << (8 * e);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hi |= f32_to_e4m3(y[k][4 + e] / s) << (8 * e);
+        for (int e = 0; e < 4; ++e)
+          hi |= f32_to_e4m3((float)((double)y[k][4 + e] * rinv)) << (8 * e);
       }
       *reinterpret_cast<u32x2_a4*>(row_out + c * kChunk) = u32x2_a4{lo, hi};
     }
@@ -130,9 +145,9 @@ __device__ __forceinline__ void normed_row(const uint16_t* __restrict__ hid,
 #pragma unroll
     for (int e = 0; e < kChunk; ++e) y[k][e] = 0.0f;
     if (c < nchunks) {
-      const uint4 hv = reinterpret_cast<const uint4*>(hid + row * H)[c];
+      const uint4 hv = ntload16(hid + row * H + c * kChunk);
       if (RES) {
-        const uint4 rv = reinterpret_cast<const uint4*>(res + row * H)[c];
+        const uint4 rv = ntload16(res + row * H + c * kChunk);
         const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
         const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
         uint32_t ow[4];
@@ -144,7 +159,8 @@ __device__ __forceinline__ void normed_row(const uint16_t* __restrict__ hid,
           y[k][2 * e] = bf16_to_f32(ow[e] & 0xFFFFu);
           y[k][2 * e + 1] = bf16_to_f32(ow[e] >> 16);
         }
-        reinterpret_cast<uint4*>(res_out + row * H)[c] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+        __builtin_nontemporal_store(u32x4_t{ow[0], ow[1], ow[2], ow[3]},
+                                    reinterpret_cast<u32x4_t*>(res_out + row * H + c * kChunk));
       } else {
         unpack8(hv, y[k]);
       }
@@ -216,7 +232,7 @@ __device__ __forceinline__ void mx_encode_store(const float (&y)[kCpt][kChunk], 
 #pragma unroll
         for (int e = 0; e < 4; ++e) hi |= f32_to_e4m3(y[k][4 + e] * inv) << (8 * e);
       }
-      *reinterpret_cast<uint2*>(codes_row + c * kChunk) = make_uint2(lo, hi);
+      __builtin_nontemporal_store(u32x2_t{lo, hi}, reinterpret_cast<u32x2_t*>(codes_row + c * kChunk));
       if ((c & 3) == 0) sh_e[c >> 2] = (uint8_t)E;
     }
   }
