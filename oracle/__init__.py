@@ -25,9 +25,11 @@ from .norm_rope import inv_rms, norm_rope
 from .producer import rmsnorm_rowmx, rmsnorm_mx
 from .mxact import mx_block_quantize, mx_block_decode
 from .layouts import bsd_to_nbsd, nbsd_to_bsd
+from .headnorm import head_norm_rope, RMS_NORM, LAYER_NORM
 
 __all__ = [
     "e4m3_decode", "e4m3_encode", "e8m0_decode", "bf16_round_f32", "bf16_to_f64", "f64_to_bf16",
     "rowmx_quantize", "rowmx_unpack", "mx_weight_quantize", "mx_weight_decode",
     "project", "segment_ssq", "inv_rms", "norm_rope", "rmsnorm_rowmx", "rmsnorm_mx", "mx_block_quantize", "mx_block_decode", "bsd_to_nbsd", "nbsd_to_bsd",
+    "head_norm_rope", "RMS_NORM", "LAYER_NORM",
 ]
