@@ -11,7 +11,7 @@ Prints ONE JSON line.  ``value`` is the projection's algorithmic TFLOP/s over th
 the library launches on, averaged over the timed steps.  ``cpu_baseline`` times the CPU oracle
 (NumPy, fp64) on a bounded row sample of the same workload on this host.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5|3|2] [--act rowmx|mx]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5|3|2] [--act rowmx|mx] [--headnorm none|rms|ln]
                     [--layout bsd|nbsd] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -32,12 +32,17 @@ METRIC = "QKV proj TFLOP/s (% MXFP8 MFMA peak) + norm/RoPE GB/s, S=75600 H=5120"
 PEAK_MXFP8_TFLOPS = 5000.0          # MI355X dense MXFP8 MFMA
 PEAK_HBM_GBS = 8000.0               # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "project_kernel_c5_traffic.json")
-PROJECT_SRC = os.path.join(ROOT, "rope_mxfp8_qkv_amd", "csrc", "project.hip")
+PROJECT_SRC = [os.path.join(ROOT, "rope_mxfp8_qkv_amd", "csrc", f)
+               for f in ("project_kernel.h", "project.hip")]
 
 
-def source_digest(path: str) -> str:
+def source_digest(paths) -> str:
+    """sha256 prefix of the projection's sources (the kernel header and its ROW_MX launcher)."""
     import hashlib
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
@@ -133,6 +138,9 @@ def parse():
     ap.add_argument("--act", choices=["rowmx", "mx"], default="rowmx",
                     help="activation encoding: ROW_MX rows with an fp32 row scale (the projection's "
                          "packed_hidden) or MX block-32 (E8M0 exponent per 32 elements)")
+    ap.add_argument("--headnorm", choices=["none", "rms", "ln"], default="none",
+                    help="per-head qk-norm (RMS_NORM / LAYER_NORM) + RoPE fused into the projection's "
+                         "epilogue instead of the across-heads norm pass (ROW_MX activations)")
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
@@ -210,6 +218,14 @@ def run_gpu(args):
     del inp["w"], codes, e8
 
     mx = args.act == "mx"
+    hn = {"none": 0, "rms": q.HEAD_RMS_NORM, "ln": q.HEAD_LAYER_NORM}[args.headnorm]
+    if hn and mx:
+        raise SystemExit("--headnorm runs on ROW_MX activations")
+    if hn:     # per-head gammas / beta: the first head_dim entries of the seeded segment draws
+        d = p.head_dim
+        hgq, hgk = inp["gq"][:d].contiguous(), inp["gk"][:d].contiguous()
+        hbq = (inp["bias"][:d].contiguous() if hn == q.HEAD_LAYER_NORM else None)
+        hbk = (inp["bias"][d:2 * d].contiguous() if hn == q.HEAD_LAYER_NORM else None)
     if mx:
         codes_a = torch.empty((T, H), dtype=torch.uint8, device=dev)
         e8_a = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
@@ -241,7 +257,13 @@ def run_gpu(args):
                                       residual=inp["res"], residual_out=res_out)
         if ev:
             ev[1].record(stream)
-        if mx:
+        if hn:
+            q.qkv_rowmx_project_headnorm(packed, wp, out, H=H, num_heads=p.num_heads,
+                                         num_kv_heads=p.num_kv_heads, head_dim=p.head_dim,
+                                         norm_kind=hn, q_gamma=hgq, k_gamma=hgk, q_beta=hbq,
+                                         k_beta=hbk, eps=1e-6, cos=inp["cos"], sin=inp["sin"],
+                                         bias=inp["bias"], workspace=ws, layout=layout)
+        elif mx:
             q.qkv_mx_project(codes_a, e8_a, wp, out, H=H, num_heads=p.num_heads,
                              num_kv_heads=p.num_kv_heads, head_dim=p.head_dim, bias=inp["bias"],
                              ssq=ssq, workspace=ws, layout=layout)
@@ -251,10 +273,11 @@ def run_gpu(args):
                                 bias=inp["bias"], ssq=ssq, workspace=ws, layout=layout)
         if ev:
             ev[2].record(stream)
-        q.qk_norm_rope_apply(out, num_heads=p.num_heads, num_kv_heads=p.num_kv_heads,
-                             head_dim=p.head_dim, eps=1e-6, flags=flags, ssq=ssq,
-                             q_gamma=inp["gq"], k_gamma=inp["gk"], cos=inp["cos"], sin=inp["sin"],
-                             layout=layout)
+        if not hn:
+            q.qk_norm_rope_apply(out, num_heads=p.num_heads, num_kv_heads=p.num_kv_heads,
+                                 head_dim=p.head_dim, eps=1e-6, flags=flags, ssq=ssq,
+                                 q_gamma=inp["gq"], k_gamma=inp["gk"], cos=inp["cos"],
+                                 sin=inp["sin"], layout=layout)
         if ev:
             ev[3].record(stream)
 
@@ -282,7 +305,7 @@ def run_gpu(args):
         "stage_ms": {"producer": float(ms[0]), "projection": float(ms[1]),
                      "norm_rope": float(ms[2])},
         "projection_tflops": proj_tflops,
-        "norm_rope_gbs": nbytes["norm_rope"] / (ms[2] * 1e-3) / 1e9,
+        "norm_rope_gbs": None if hn else nbytes["norm_rope"] / (ms[2] * 1e-3) / 1e9,
         "producer_gbs": (nbytes["producer"] / (ms[0] * 1e-3) / 1e9) if inp["producer"] else None,
         "flops": flops,
         "bytes": nbytes,
@@ -290,6 +313,7 @@ def run_gpu(args):
         "p": p,
         "producer": inp["producer"],
         "mx": mx,
+        "headnorm": args.headnorm,
     }
     return res
 
@@ -367,8 +391,11 @@ def main():
         "dtype": "mxfp8 (e4m3 x e4m3 -> fp32 MFMA), fp32 norm/RoPE, bf16 I/O",
         "data": "synthetic",
         "config": {
-            "workload": ("producer + QKV projection + across-heads norm + 3-axis RoPE"
-                         if r["producer"] else "QKV projection + across-heads norm + RoPE")
+            "workload": (("producer + QKV projection with per-head %s + 3-axis RoPE fused"
+                          % {"rms": "RMS_NORM", "ln": "LAYER_NORM"}[r["headnorm"]])
+                         if r["headnorm"] != "none" else
+                         ("producer + QKV projection + across-heads norm + 3-axis RoPE"
+                          if r["producer"] else "QKV projection + across-heads norm + RoPE"))
                         + (", MX block-32 activations" if r["mx"] else ", ROW_MX activations"),
             "T": p.T, "H": p.H, "I": p.I, "num_heads": p.num_heads,
             "num_kv_heads": p.num_kv_heads, "head_dim": p.head_dim,
@@ -376,7 +403,10 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": ("qkv_mx_project (project_kernel + ssq_reduce)" if r["mx"] else
+            "kernel": ("qkv_mx_project (activation repacks + project_kernel + ssq_reduce)"
+                       if r["mx"] else
+                       "qkv_rowmx_project_headnorm (activation repack + project_kernel)"
+                       if r["headnorm"] != "none" else
                        "qkv_rowmx_project (activation repack + project_kernel + ssq_reduce)"),
             "bound": "mfma",
             "achieved": ach,
@@ -384,13 +414,13 @@ def main():
             "unit": "TFLOP/s",
             "frac": ach / PEAK_MXFP8_TFLOPS,
             "traffic": (measured_traffic() if args.config == 5 and args.layout == "bsd"
-                        and not r["mx"] else None),
+                        and not r["mx"] and r["headnorm"] == "none" else None),
         },
         "stages": {
             "ms": r["stage_ms"],
             "projection_tflops": r["projection_tflops"],
             "norm_rope_gbs": r["norm_rope_gbs"],
-            "norm_rope_hbm_frac": r["norm_rope_gbs"] / PEAK_HBM_GBS,
+            "norm_rope_hbm_frac": (r["norm_rope_gbs"] / PEAK_HBM_GBS) if r["norm_rope_gbs"] else None,
             "producer_gbs": r["producer_gbs"],
             "producer_hbm_frac": (r["producer_gbs"] / PEAK_HBM_GBS) if r["producer_gbs"] else None,
         },

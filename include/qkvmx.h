@@ -59,6 +59,10 @@ enum {
   QKVMX_LAYOUT_NBSD = 1   /* [I / head_dim, T, head_dim]: (h, t, j) at (h * T + t) * d + j    */
 };
 
+/* Per-head qk-norm kinds of qkv_rowmx_project_headnorm ([QKV-CTE] "Upstream behavior":
+ * RMS_NORM / LAYER_NORM). */
+enum { QKVMX_HEAD_RMS_NORM = 1, QKVMX_HEAD_LAYER_NORM = 2 };
+
 /* Element types of the plain row quantiser's input. */
 enum { QKVMX_DTYPE_F32 = 0, QKVMX_DTYPE_BF16 = 1 };
 
@@ -179,6 +183,38 @@ qkvmx_status qkv_rowmx_project(const uint8_t* a_codes, int64_t a_row_stride,
                                int32_t num_kv_heads, int32_t head_dim, int32_t layout,
                                uint16_t* out, float* ssq, void* workspace, size_t ws_bytes,
                                hipStream_t stream);
+
+/* Pass 1 with the upstream per-head qk-norm and rotate-half RoPE fused into the epilogue
+ * ([QKV-CTE] "Upstream behavior": an optional per-head qk-norm (RMS_NORM / LAYER_NORM) and
+ * rotate-half RoPE applied as each finished result leaves the accumulators, with the dequant
+ * scaling and the bias add, so no second pass over Q and K is needed; "Design 1)": each head's
+ * d_head slice normalised by its own statistics).  With X the dequantised, bias-added fp32 value
+ * of qkv_rowmx_project (before rounding), for every Q and K head h of token t:
+ *   RMS_NORM:   y = X / sqrt(mean_h(X^2) + eps) * gamma
+ *   LAYER_NORM: y = (X - mean_h(X)) / sqrt(mean_h((X - mean_h(X))^2) + eps) * gamma + beta
+ * (statistics over the head's d values), then, with cos_tab / sin_tab, rotate-half RoPE of each
+ * pair (j, j + d/2), j < d/2, by the angle of position j of row t:
+ *   out_j = y_j cos[t, j] - y_{j+d/2} sin[t, j],  out_{j+d/2} = y_{j+d/2} cos[t, j] + y_j sin[t, j]
+ * (rotate-half tables hold the same angle in both halves; the second half is not read).  V is
+ * stored as X.  The result is rounded to bf16 once, in `layout` (as qkv_rowmx_project).
+ *   q_gamma, k_gamma   bf16 [head_dim], one per segment, shared by its heads; k_gamma required
+ *                      iff num_kv_heads > 0.
+ *   q_beta, k_beta     bf16 [head_dim] or NULL (0); QKVMX_HEAD_LAYER_NORM only.
+ *   cos_tab, sin_tab   fp32 [T, head_dim], both or neither (NULL: no RoPE).
+ *   workspace          >= qkvmx_workspace_bytes(T, H, I) bytes, 256-byte aligned; scratch.
+ * Activation arguments as qkv_rowmx_project; no channel scale, no sums of squares.  Requires
+ * head_dim 64 or 128 and num_heads * head_dim, num_kv_heads * head_dim multiples of 128
+ * (QKVMX_ERR_UNSUPPORTED otherwise); gamma/beta 8-byte, tables 16-byte aligned. */
+qkvmx_status qkv_rowmx_project_headnorm(const uint8_t* a_codes, int64_t a_row_stride,
+                                         const uint8_t* a_scales, int64_t a_scale_stride,
+                                         const void* w_packed, const uint16_t* bias, int64_t T,
+                                         int64_t H, int32_t num_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t layout, int32_t norm_kind,
+                                         const uint16_t* q_gamma, const uint16_t* k_gamma,
+                                         const uint16_t* q_beta, const uint16_t* k_beta,
+                                         float eps, const float* cos_tab, const float* sin_tab,
+                                         uint16_t* out, void* workspace, size_t ws_bytes,
+                                         hipStream_t stream);
 
 /* Workspace bytes qkv_mx_project needs for a [T, H] x [H, I] call: the activation codes and
  * their exponents re-laid in the kernel's LDS stage images (about T * H * 33 / 32 bytes) plus

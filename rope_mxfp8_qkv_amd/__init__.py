@@ -13,15 +13,16 @@ import os
 from typing import Optional
 
 from . import _abi
-from ._abi import (NORM_Q, NORM_K, FUSED_ROPE, LAYOUT_BSD, LAYOUT_NBSD, DTYPE_F32, DTYPE_BF16, QkvmxError,
-                   lib, lib_path)
+from ._abi import (NORM_Q, NORM_K, FUSED_ROPE, LAYOUT_BSD, LAYOUT_NBSD, DTYPE_F32, DTYPE_BF16,
+                   HEAD_RMS_NORM, HEAD_LAYER_NORM, QkvmxError, lib, lib_path)
 
 __all__ = [
     "NORM_Q", "NORM_K", "FUSED_ROPE", "LAYOUT_BSD", "LAYOUT_NBSD", "DTYPE_F32", "DTYPE_BF16", "QkvmxError",
     "lib", "lib_path", "mx_weight_quantize", "qkv_weight_packed_bytes", "qkv_weight_prepack",
     "row_quantize_packed", "rmsnorm_mx_quantize", "qkvmx_workspace_bytes", "qkv_rowmx_project",
     "qk_norm_rope_apply", "prepare_weight", "mx_block_quantize", "rmsnorm_mx_block_quantize",
-    "qkv_mx_workspace_bytes", "qkv_mx_project",
+    "qkv_mx_workspace_bytes", "qkv_mx_project", "qkv_rowmx_project_headnorm", "HEAD_RMS_NORM",
+    "HEAD_LAYER_NORM",
 ]
 
 
@@ -161,6 +162,27 @@ def qkv_rowmx_project(packed_a, w_packed, out, *, H: int, num_heads: int, num_kv
                                    _ptr(bias), T, H, num_heads, num_kv_heads, head_dim, layout,
                                    _ptr(out), _ptr(ssq), ws_ptr, ws_n, _stream(stream)),
            "qkv_rowmx_project")
+
+
+def qkv_rowmx_project_headnorm(packed_a, w_packed, out, *, H: int, num_heads: int,
+                               num_kv_heads: int, head_dim: int, norm_kind: int, q_gamma,
+                               k_gamma=None, q_beta=None, k_beta=None, eps: float = 1e-6,
+                               cos=None, sin=None, bias=None, workspace=None,
+                               layout: int = LAYOUT_BSD, stream=None):
+    """Pass 1 on packed ROW_MX rows [T, H + 4] with the per-head qk-norm (HEAD_RMS_NORM or
+    HEAD_LAYER_NORM, gamma / beta [head_dim]) and optional rotate-half RoPE fused into the
+    epilogue."""
+    T = packed_a.shape[0]
+    a_ptr = _ptr(packed_a)
+    rs = packed_a.shape[1]
+    ws_ptr, ws_n = (None, 0) if workspace is None else (_ptr(workspace),
+                                                        workspace.numel() * workspace.element_size())
+    _check(lib().qkv_rowmx_project_headnorm(a_ptr, rs, a_ptr + H, rs, _ptr(w_packed), _ptr(bias),
+                                            T, H, num_heads, num_kv_heads, head_dim, layout,
+                                            norm_kind, _ptr(q_gamma), _ptr(k_gamma), _ptr(q_beta),
+                                            _ptr(k_beta), float(eps), _ptr(cos), _ptr(sin),
+                                            _ptr(out), ws_ptr, ws_n, _stream(stream)),
+           "qkv_rowmx_project_headnorm")
 
 
 def qk_norm_rope_apply(qkv, *, num_heads: int, num_kv_heads: int, head_dim: int, eps: float,

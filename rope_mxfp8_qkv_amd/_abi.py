@@ -10,6 +10,8 @@ NORM_K = 2
 FUSED_ROPE = 4
 LAYOUT_BSD = 0
 LAYOUT_NBSD = 1
+HEAD_RMS_NORM = 1
+HEAD_LAYER_NORM = 2
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 
@@ -40,6 +42,9 @@ SIGNATURES = {
     "rmsnorm_mx_block_quantize": (c_i32, [c_vp, c_vp, c_vp, c_f, c_i64, c_i64, c_i64, c_vp, c_vp,
                                           c_vp, c_vp, c_vp]),
     "qkv_mx_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64]),
+    "qkv_rowmx_project_headnorm": (c_i32, [c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_i64, c_i32,
+                                           c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_f,
+                                           c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "qkv_mx_project": (c_i32, [c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_i64, c_i64, c_i32,
                                c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "qk_norm_rope_apply": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_i32, c_i32,

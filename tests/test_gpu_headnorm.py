@@ -1,0 +1,90 @@
+"""GPU parity of the projection with the per-head qk-norm (RMS_NORM / LAYER_NORM) and
+rotate-half RoPE fused into its epilogue ([QKV-CTE] "Upstream behavior"), against the oracle's
+pass 1 followed by its per-head norm and RoPE (fp64, one bf16 rounding on the GPU side only).
+Covers head_dim 64 and 128, LayerNorm with and without beta, RoPE on and off, GQA, a single
+segment, ragged T and I, T = 1 and both output layouts; and the unsupported shapes."""
+import numpy as np
+import pytest
+
+import gpu_common as G
+import oracle
+import synth
+from oracle import codecs
+
+pytestmark = pytest.mark.gpu
+
+RMS, LN = 1, 2
+CASES = [
+    # name, projection, kind, rope, beta, layout
+    ("d64-rms-rope", G.custom_projection("hn1", T=128, H=256, nq=2, nkv=2, d=64), RMS, True, False, "bsd"),
+    ("d128-ln-beta-rope-nbsd", G.custom_projection("hn2", T=300, H=512, nq=3, nkv=1, d=128), LN, True, True, "nbsd"),
+    ("d64-rms-T1", G.custom_projection("hn3", T=1, H=256, nq=2, nkv=2, d=64), RMS, False, False, "bsd"),
+    ("single-seg-ln", G.custom_projection("hn4", T=257, H=1024, nq=4, nkv=0, d=128, rope="1d"), LN, True, False, "bsd"),
+    ("gqa-d128-rms", G.custom_projection("hn5", T=700, H=1024, nq=8, nkv=2, d=128), RMS, True, False, "bsd"),
+    ("d64-ln-nbsd", G.custom_projection("hn6", T=130, H=512, nq=6, nkv=2, d=64), LN, False, True, "nbsd"),
+]
+
+
+@pytest.mark.parametrize("name,p,kind,rope,beta,layout", CASES, ids=[c[0] for c in CASES])
+def test_headnorm_parity(name, p, kind, rope, beta, layout):
+    import torch
+    import rope_mxfp8_qkv_amd as q
+    q.lib()
+    dev = G.torch_dev()
+    inp = G.make_inputs(p)
+    d = p.head_dim
+    rng = np.random.default_rng(17)
+    gq = codecs.f64_to_bf16(1 + 0.1 * rng.standard_normal(d))
+    gk = codecs.f64_to_bf16(1 + 0.1 * rng.standard_normal(d)) if p.num_kv_heads else None
+    bq = codecs.f64_to_bf16(0.1 * rng.standard_normal(d)) if beta else None
+    bk = codecs.f64_to_bf16(0.1 * rng.standard_normal(d)) if beta and p.num_kv_heads else None
+    cos, sin = (inp.cos, inp.sin) if rope else (None, None)
+    codes, sA = oracle.rowmx_unpack(inp.packed, p.H)
+    X, _ = oracle.project(codes, sA, inp.w_codes, inp.w_e8m0, None, inp.bias,
+                          num_heads=p.num_heads, num_kv_heads=p.num_kv_heads, head_dim=d)
+    ref = oracle.head_norm_rope(X, kind, gq, gk, 1e-6, cos, sin, num_heads=p.num_heads,
+                                num_kv_heads=p.num_kv_heads, head_dim=d, q_beta_bf16=bq,
+                                k_beta_bf16=bk)
+    wp = q.prepare_weight(G.to_dev(inp.w_codes, dev), G.to_dev(inp.w_e8m0, dev), p.H, p.I)
+    shape = (p.I // d, p.T, d) if layout == "nbsd" else (p.T, p.I)
+    out = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(q.qkvmx_workspace_bytes(p.T, p.H, p.I), dtype=torch.uint8, device=dev)
+    opt = lambda a: None if a is None else G.bf16_dev(a, dev)
+    q.qkv_rowmx_project_headnorm(G.to_dev(inp.packed, dev), wp, out, H=p.H,
+                                 num_heads=p.num_heads, num_kv_heads=p.num_kv_heads, head_dim=d,
+                                 norm_kind=kind, q_gamma=opt(gq), k_gamma=opt(gk),
+                                 q_beta=opt(bq), k_beta=opt(bk), eps=1e-6,
+                                 cos=None if cos is None else G.to_dev(cos, dev),
+                                 sin=None if sin is None else G.to_dev(sin, dev),
+                                 bias=G.bf16_dev(inp.bias, dev), workspace=ws,
+                                 layout=q.LAYOUT_NBSD if layout == "nbsd" else q.LAYOUT_BSD)
+    torch.cuda.synchronize()
+    got = G.bf16_host(out)
+    if layout == "nbsd":
+        got = oracle.nbsd_to_bsd(got)
+    G.check_close(got, ref, f"{name} output")
+
+
+def test_headnorm_unsupported_shapes():
+    import torch
+    import rope_mxfp8_qkv_amd as q
+    q.lib()
+    dev = G.torch_dev()
+    buf = torch.zeros(1 << 20, dtype=torch.uint8, device=dev)
+    g = torch.ones(128, dtype=torch.bfloat16, device=dev)
+    out = torch.empty((4, 512), dtype=torch.bfloat16, device=dev)
+    wp = torch.zeros(q.qkv_weight_packed_bytes(256, 512), dtype=torch.uint8, device=dev)
+    packed = torch.zeros((4, 260), dtype=torch.uint8, device=dev)
+    with pytest.raises(q.QkvmxError) as ei:           # head_dim 32
+        q.qkv_rowmx_project_headnorm(packed, wp, out, H=256, num_heads=8, num_kv_heads=4,
+                                     head_dim=32, norm_kind=1, q_gamma=g, k_gamma=g, workspace=buf)
+    assert ei.value.status == 6
+    with pytest.raises(q.QkvmxError) as ei:           # Q segment of 192 channels
+        q.qkv_rowmx_project_headnorm(packed, wp, out, H=256, num_heads=3, num_kv_heads=1,
+                                     head_dim=64, norm_kind=1, q_gamma=g, k_gamma=g, workspace=buf)
+    assert ei.value.status == 6
+    with pytest.raises(q.QkvmxError) as ei:           # beta with RMS_NORM
+        q.qkv_rowmx_project_headnorm(packed, wp, out, H=256, num_heads=2, num_kv_heads=1,
+                                     head_dim=128, norm_kind=1, q_gamma=g, k_gamma=g, q_beta=g,
+                                     workspace=buf)
+    assert ei.value.status == 4
