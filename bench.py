@@ -45,15 +45,19 @@ def source_digest(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per projection launch from the committed counter summary, or None when the
-    kernel source changed since the counters were taken."""
+def measured_traffic(kernels):
+    """HBM bytes per projection call (the sum over `kernels`, the kernels the call launches)
+    from the committed counter summary, or None when the kernel source changed since the
+    counters were taken or a kernel is missing from it."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     rec = json.load(open(TRAFFIC_FILE))
     if rec.get("kernel_src_sha256_16") != source_digest(PROJECT_SRC):
         return None
-    return rec["hbm_bytes_per_launch"]
+    per = rec.get("per_kernel", {})
+    if any(k not in per for k in kernels):
+        return None
+    return sum(per[k]["read_bytes"] + per[k]["write_bytes"] for k in kernels)
 
 
 def copy_calibration(nbytes: int):
@@ -69,6 +73,7 @@ def copy_calibration(nbytes: int):
 
 
 PROJECTION_KERNELS = ("act_repack_kernel", "project_kernel", "ssq_reduce_kernel")
+STAGED_KERNELS = ("project_kernel", "ssq_reduce_kernel")   # + a 1-block counter reset
 
 
 def _counter_means(run_dir: str, counter: str):
@@ -111,18 +116,20 @@ def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy
            "ssq_reduce_kernel": (4 * T * 2 * ((p.Iq + p.Ik) // 128), 8 * T)}
     per = {}
     for k in PROJECTION_KERNELS:
+        if k not in fk or k not in wk:
+            continue
         per[k] = {"fetch_kib": fk[k], "write_kib": wk[k],
                   "read_bytes": fk[k] * 1024 * fetch_scale, "write_bytes": wk[k] * 1024 * write_scale,
                   "alg_read_bytes": alg[k][0], "alg_write_bytes": alg[k][1]}
-    rec = {"what": f"HBM bytes per qkv_rowmx_project launch ({' + '.join(PROJECTION_KERNELS)}) at "
+    rec = {"what": f"HBM bytes per dispatch of the projection's kernels ({', '.join(per)}) at "
                    f"T={T} H={H} I={I}, from rocprofv3 FETCH_SIZE/WRITE_SIZE scaled by a "
                    f"{copy_bytes}-byte copy calibration (copy kernel {ck})",
            "kernel_src_sha256_16": source_digest(PROJECT_SRC),
            "fetch_scale": fetch_scale, "write_scale": write_scale, "per_kernel": per,
-           "hbm_bytes_per_launch": sum(v["read_bytes"] + v["write_bytes"] for v in per.values())}
+           "hbm_bytes_per_call": sum(v["read_bytes"] + v["write_bytes"] for v in per.values())}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
-    print(json.dumps({"traffic_file": TRAFFIC_FILE, "hbm_bytes_per_launch": rec["hbm_bytes_per_launch"],
+    print(json.dumps({"traffic_file": TRAFFIC_FILE, "hbm_bytes_per_call": rec["hbm_bytes_per_call"],
                       "fetch_scale": fetch_scale, "write_scale": write_scale}))
 
 
@@ -135,6 +142,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layout", choices=["bsd", "nbsd"], default="bsd",
                     help="output layout of the projection and pass 2 (BSD [T, I] or NBSd [I/d, T, d])")
+    ap.add_argument("--act-layout", choices=["staged", "packed"], default="staged",
+                    help="ROW_MX hand-over between producer and projection: codes written by the "
+                         "producer in the projection's stage-image layout with fp32 row scales "
+                         "(staged), or the pages' packed [T, H + 4] rows re-laid by the "
+                         "projection on every call (packed)")
     ap.add_argument("--act", choices=["rowmx", "mx"], default="rowmx",
                     help="activation encoding: ROW_MX rows with an fp32 row scale (the projection's "
                          "packed_hidden) or MX block-32 (E8M0 exponent per 32 elements)")
@@ -229,19 +241,26 @@ def run_gpu(args):
     if mx:
         codes_a = torch.empty((T, H), dtype=torch.uint8, device=dev)
         e8_a = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
-    else:
+    staged = not mx and not hn and args.act_layout == "staged"
+    if staged:
+        img = torch.empty(q.qkv_act_image_bytes(T, H), dtype=torch.uint8, device=dev)
+        row_scale = torch.empty((T,), dtype=torch.float32, device=dev)
+    elif not mx:
         packed = torch.empty((T, H + 4), dtype=torch.uint8, device=dev)
     res_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if inp["producer"] else None
     layout = q.LAYOUT_NBSD if args.layout == "nbsd" else q.LAYOUT_BSD
     out = (torch.empty((I // p.head_dim, T, p.head_dim), dtype=torch.bfloat16, device=dev)
            if args.layout == "nbsd" else torch.empty((T, I), dtype=torch.bfloat16, device=dev))
     ssq = torch.empty((T, 2), dtype=torch.float32, device=dev)
-    ws_n = q.qkv_mx_workspace_bytes(T, H, I) if mx else q.qkvmx_workspace_bytes(T, H, I)
+    ws_n = (q.qkv_mx_workspace_bytes(T, H, I) if mx else
+            q.qkv_staged_workspace_bytes(T, I) if staged else q.qkvmx_workspace_bytes(T, H, I))
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
     flags = q.NORM_Q | q.NORM_K | q.FUSED_ROPE
     if not inp["producer"]:                         # activations fixed for the whole run
         if mx:
             q.mx_block_quantize(inp["x"], codes_a, e8_a)
+        elif staged:
+            q.row_quantize_staged(inp["x"], img, row_scale)
         else:
             q.row_quantize_packed(inp["x"], packed)
 
@@ -252,6 +271,9 @@ def run_gpu(args):
             if mx:
                 q.rmsnorm_mx_block_quantize(inp["hid"], inp["pgamma"], 1e-6, codes_a, e8_a,
                                             residual=inp["res"], residual_out=res_out)
+            elif staged:
+                q.rmsnorm_mx_quantize_staged(inp["hid"], inp["pgamma"], 1e-6, img, row_scale,
+                                             residual=inp["res"], residual_out=res_out)
             else:
                 q.rmsnorm_mx_quantize(inp["hid"], inp["pgamma"], 1e-6, packed,
                                       residual=inp["res"], residual_out=res_out)
@@ -263,6 +285,10 @@ def run_gpu(args):
                                          norm_kind=hn, q_gamma=hgq, k_gamma=hgk, q_beta=hbq,
                                          k_beta=hbk, eps=1e-6, cos=inp["cos"], sin=inp["sin"],
                                          bias=inp["bias"], workspace=ws, layout=layout)
+        elif staged:
+            q.qkv_rowmx_project_staged(img, row_scale, wp, out, H=H, num_heads=p.num_heads,
+                                       num_kv_heads=p.num_kv_heads, head_dim=p.head_dim,
+                                       bias=inp["bias"], ssq=ssq, workspace=ws, layout=layout)
         elif mx:
             q.qkv_mx_project(codes_a, e8_a, wp, out, H=H, num_heads=p.num_heads,
                              num_kv_heads=p.num_kv_heads, head_dim=p.head_dim, bias=inp["bias"],
@@ -313,6 +339,7 @@ def run_gpu(args):
         "p": p,
         "producer": inp["producer"],
         "mx": mx,
+        "staged": staged,
         "headnorm": args.headnorm,
     }
     return res
@@ -396,7 +423,9 @@ def main():
                          if r["headnorm"] != "none" else
                          ("producer + QKV projection + across-heads norm + 3-axis RoPE"
                           if r["producer"] else "QKV projection + across-heads norm + RoPE"))
-                        + (", MX block-32 activations" if r["mx"] else ", ROW_MX activations"),
+                        + (", MX block-32 activations" if r["mx"] else
+                           ", ROW_MX activations staged in the projection's operand layout"
+                           if r["staged"] else ", ROW_MX activations as packed [T, H+4] rows"),
             "T": p.T, "H": p.H, "I": p.I, "num_heads": p.num_heads,
             "num_kv_heads": p.num_kv_heads, "head_dim": p.head_dim,
             "grid": list(p.grid) if p.grid else None, "layout": args.layout.upper().replace("NBSD", "NBSd"),
@@ -407,14 +436,17 @@ def main():
                        if r["mx"] else
                        "qkv_rowmx_project_headnorm (activation repack + project_kernel)"
                        if r["headnorm"] != "none" else
+                       "qkv_rowmx_project_staged (counter reset + project_kernel + ssq_reduce)"
+                       if r["staged"] else
                        "qkv_rowmx_project (activation repack + project_kernel + ssq_reduce)"),
             "bound": "mfma",
             "achieved": ach,
             "peak": PEAK_MXFP8_TFLOPS,
             "unit": "TFLOP/s",
             "frac": ach / PEAK_MXFP8_TFLOPS,
-            "traffic": (measured_traffic() if args.config == 5 and args.layout == "bsd"
-                        and not r["mx"] and r["headnorm"] == "none" else None),
+            "traffic": (measured_traffic(STAGED_KERNELS if r["staged"] else PROJECTION_KERNELS)
+                        if args.config == 5 and args.layout == "bsd" and not r["mx"]
+                        and r["headnorm"] == "none" else None),
         },
         "stages": {
             "ms": r["stage_ms"],

@@ -124,6 +124,37 @@ qkvmx_status rmsnorm_mx_quantize(const uint16_t* hidden, const uint16_t* residua
                                  int64_t unpadded_H, uint16_t* residual_out, uint8_t* packed_out,
                                  hipStream_t stream);
 
+/* Staged ROW_MX activations.  [RMSNORM-MX] lays its quantised output out for the consumer
+ * that reads it next (its scale packing and H-swizzle serve the other machine's transposes);
+ * the counterpart here is the projection's own operand layout, so the projection DMA-copies
+ * the codes into LDS without re-laying them per call.  The arithmetic (scale, codes) is exactly
+ * that of the packed-row producers; only the placement of the bytes differs:
+ *   act_image  [ceil(T / 256)][KS][256][64] bytes, KS = 4 * ceil(H / 256): the code of row t,
+ *              element h sits at ((t / 256 * KS + h / 64) * 256 + t % 256) * 64
+ *              + ((((h / 16) % 4) ^ sw(t % 256)) << 4) + h % 16,
+ *              sw(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1).  Codes for h in [H, 64 KS) and every
+ *              code of rows t in [T, 256 ceil(T / 256)) are written as 0x00.
+ *              qkv_act_image_bytes(T, H) bytes, 16-byte aligned.
+ *   row_scale  [T] fp32: the row scale s of the packed layout's 4-byte tail. */
+size_t qkv_act_image_bytes(int64_t T, int64_t H);
+
+/* row_quantize_packed with the staged output (act_image, row_scale as above).  image_bytes
+ * must be >= qkv_act_image_bytes(T, H).  Requires H % 32 == 0, H <= 16384; x 16-byte,
+ * act_image 16-byte, row_scale 4-byte aligned. */
+qkvmx_status row_quantize_staged(const void* x, int32_t x_dtype, int64_t T, int64_t H,
+                                 uint8_t* act_image, size_t image_bytes, float* row_scale,
+                                 hipStream_t stream);
+
+/* rmsnorm_mx_quantize with the staged output: the same r, inv, y, scale and codes; codes into
+ * act_image, scales into row_scale (layouts above).  image_bytes >= qkv_act_image_bytes(T, H).
+ * Other arguments and requirements as rmsnorm_mx_quantize; act_image 16-byte, row_scale 4-byte
+ * aligned. */
+qkvmx_status rmsnorm_mx_quantize_staged(const uint16_t* hidden, const uint16_t* residual,
+                                        const uint16_t* gamma, float eps, int64_t T, int64_t H,
+                                        int64_t unpadded_H, uint16_t* residual_out,
+                                        uint8_t* act_image, size_t image_bytes, float* row_scale,
+                                        hipStream_t stream);
+
 /* MX block-32 encoding of activation rows ([RMSNORM-MX] qmx_output_dtype: E4M3 codes with one
  * E8M0 scale per 32 elements of a row; the other machine's packing and swizzle of the scales are
  * not reproduced).  x: [T, H] fp32 or bf16 (x_dtype).  codes_out: [T, H] bytes, natural H order;
@@ -183,6 +214,25 @@ qkvmx_status qkv_rowmx_project(const uint8_t* a_codes, int64_t a_row_stride,
                                int32_t num_kv_heads, int32_t head_dim, int32_t layout,
                                uint16_t* out, float* ssq, void* workspace, size_t ws_bytes,
                                hipStream_t stream);
+
+/* Workspace bytes qkv_rowmx_project_staged needs: the per-tile sums of squares and the tile
+ * counters (no activation re-layout).  0 for invalid sizes. */
+size_t qkv_staged_workspace_bytes(int64_t T, int64_t I);
+
+/* qkv_rowmx_project on staged activations (act_image, row_scale written by
+ * row_quantize_staged or rmsnorm_mx_quantize_staged for the same T and H): the same out and
+ * ssq, bit for bit, as qkv_rowmx_project on the packed rows of the same codes and scales.
+ *   image_bytes  >= qkv_act_image_bytes(T, H); act_image 256-byte aligned.
+ *   workspace    >= qkv_staged_workspace_bytes(T, I) bytes, 256-byte aligned, required;
+ *                scratch, as for qkv_rowmx_project.
+ * Other arguments, layouts and errors as qkv_rowmx_project. */
+qkvmx_status qkv_rowmx_project_staged(const uint8_t* act_image, size_t image_bytes,
+                                      const float* row_scale, const void* w_packed,
+                                      const float* w_channel_scale, const uint16_t* bias,
+                                      int64_t T, int64_t H, int32_t num_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t layout,
+                                      uint16_t* out, float* ssq, void* workspace,
+                                      size_t ws_bytes, hipStream_t stream);
 
 /* Pass 1 with the upstream per-head qk-norm and rotate-half RoPE fused into the epilogue
  * ([QKV-CTE] "Upstream behavior": an optional per-head qk-norm (RMS_NORM / LAYER_NORM) and

@@ -22,7 +22,8 @@ __all__ = [
     "row_quantize_packed", "rmsnorm_mx_quantize", "qkvmx_workspace_bytes", "qkv_rowmx_project",
     "qk_norm_rope_apply", "prepare_weight", "mx_block_quantize", "rmsnorm_mx_block_quantize",
     "qkv_mx_workspace_bytes", "qkv_mx_project", "qkv_rowmx_project_headnorm", "HEAD_RMS_NORM",
-    "HEAD_LAYER_NORM",
+    "HEAD_LAYER_NORM", "qkv_act_image_bytes", "row_quantize_staged", "rmsnorm_mx_quantize_staged",
+    "qkv_staged_workspace_bytes", "qkv_rowmx_project_staged",
 ]
 
 
@@ -91,6 +92,38 @@ def rmsnorm_mx_quantize(hidden, gamma, eps: float, packed_out, residual=None, re
     _check(lib().rmsnorm_mx_quantize(_ptr(hidden), _ptr(residual), _ptr(gamma), float(eps), T, H,
                                      unpadded_h, _ptr(residual_out), _ptr(packed_out),
                                      _stream(stream)), "rmsnorm_mx_quantize")
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def qkv_act_image_bytes(T: int, H: int) -> int:
+    """Bytes of the staged activation image of T rows of H codes."""
+    return int(lib().qkv_act_image_bytes(T, H))
+
+
+def row_quantize_staged(x, act_image, row_scale, stream=None):
+    """x [T, H] fp32 or bf16 -> ROW_MX codes in the staged image layout (uint8, at least
+    qkv_act_image_bytes(T, H) bytes) and fp32 row scales [T]."""
+    import torch
+    T, H = x.shape
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise QkvmxError("row_quantize_staged takes fp32 or bf16 rows")
+    dt = DTYPE_BF16 if x.dtype == torch.bfloat16 else DTYPE_F32
+    _check(lib().row_quantize_staged(_ptr(x), dt, T, H, _ptr(act_image), _nbytes(act_image),
+                                     _ptr(row_scale), _stream(stream)), "row_quantize_staged")
+
+
+def rmsnorm_mx_quantize_staged(hidden, gamma, eps: float, act_image, row_scale, residual=None,
+                               residual_out=None, unpadded_h: int = 0, stream=None):
+    """bf16 hidden [T, H] (+ residual) -> residual_out (bf16), ROW_MX codes in the staged image
+    layout and fp32 row scales [T]."""
+    T, H = hidden.shape
+    _check(lib().rmsnorm_mx_quantize_staged(_ptr(hidden), _ptr(residual), _ptr(gamma), float(eps),
+                                            T, H, unpadded_h, _ptr(residual_out), _ptr(act_image),
+                                            _nbytes(act_image), _ptr(row_scale), _stream(stream)),
+           "rmsnorm_mx_quantize_staged")
 
 
 def mx_block_quantize(x, codes_out, e8m0_out, stream=None):
@@ -162,6 +195,24 @@ def qkv_rowmx_project(packed_a, w_packed, out, *, H: int, num_heads: int, num_kv
                                    _ptr(bias), T, H, num_heads, num_kv_heads, head_dim, layout,
                                    _ptr(out), _ptr(ssq), ws_ptr, ws_n, _stream(stream)),
            "qkv_rowmx_project")
+
+
+def qkv_staged_workspace_bytes(T: int, I: int) -> int:
+    return int(lib().qkv_staged_workspace_bytes(T, I))
+
+
+def qkv_rowmx_project_staged(act_image, row_scale, w_packed, out, *, H: int, num_heads: int,
+                             num_kv_heads: int, head_dim: int, channel_scale=None, bias=None,
+                             ssq=None, workspace=None, layout: int = LAYOUT_BSD, stream=None):
+    """Pass 1 on staged ROW_MX activations (``act_image`` from a staged producer, fp32
+    ``row_scale`` [T]); T is taken from ``row_scale``.  Output as qkv_rowmx_project."""
+    T = row_scale.shape[0]
+    ws_ptr, ws_n = (None, 0) if workspace is None else (_ptr(workspace), _nbytes(workspace))
+    _check(lib().qkv_rowmx_project_staged(_ptr(act_image), _nbytes(act_image), _ptr(row_scale),
+                                          _ptr(w_packed), _ptr(channel_scale), _ptr(bias), T, H,
+                                          num_heads, num_kv_heads, head_dim, layout, _ptr(out),
+                                          _ptr(ssq), ws_ptr, ws_n, _stream(stream)),
+           "qkv_rowmx_project_staged")
 
 
 def qkv_rowmx_project_headnorm(packed_a, w_packed, out, *, H: int, num_heads: int,

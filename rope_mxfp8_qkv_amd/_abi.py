@@ -47,6 +47,13 @@ SIGNATURES = {
                                            c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "qkv_mx_project": (c_i32, [c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_i64, c_i64, c_i32,
                                c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "qkv_act_image_bytes": (c_sz, [c_i64, c_i64]),
+    "row_quantize_staged": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_vp, c_sz, c_vp, c_vp]),
+    "rmsnorm_mx_quantize_staged": (c_i32, [c_vp, c_vp, c_vp, c_f, c_i64, c_i64, c_i64, c_vp, c_vp,
+                                           c_sz, c_vp, c_vp]),
+    "qkv_staged_workspace_bytes": (c_sz, [c_i64, c_i64]),
+    "qkv_rowmx_project_staged": (c_i32, [c_vp, c_sz, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i32,
+                                         c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "qk_norm_rope_apply": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_i32, c_i32,
                                    c_f, c_u32, c_i32, c_vp]),
 }

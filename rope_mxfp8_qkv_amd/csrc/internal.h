@@ -82,6 +82,16 @@ inline size_t mx_workspace_total_bytes(int64_t T, int64_t H, int64_t I) {
   return mx_counters_offset(T, H, I) + kCounterBytes;
 }
 
+// Projection on staged activations (codes already in the stage-image layout, written by a
+// staged producer): the workspace holds only the sum-of-squares partials [P][T][2] fp32 and,
+// after them, the 256-byte counter block.
+inline size_t staged_counters_offset(int64_t T, int64_t I) {
+  return (partials_bytes(T, I) + 255) / 256 * 256;
+}
+inline size_t staged_workspace_total_bytes(int64_t T, int64_t I) {
+  return staged_counters_offset(T, I) + kCounterBytes;
+}
+
 hipError_t launch_mx_weight_quantize(const float* w, int64_t H, int64_t I, uint8_t* codes,
                                      uint8_t* e8m0, hipStream_t s);
 hipError_t launch_weight_prepack(const uint8_t* codes, const uint8_t* e8m0, int64_t H, int64_t I,
@@ -91,6 +101,17 @@ hipError_t launch_row_quantize(const void* x, int dtype, int64_t T, int64_t H, u
 hipError_t launch_rmsnorm_quantize(const uint16_t* hid, const uint16_t* res, const uint16_t* gamma,
                                    float eps, int64_t T, int64_t H, int64_t Hu, uint16_t* res_out,
                                    uint8_t* packed, hipStream_t s);
+hipError_t launch_row_quantize_staged(const void* x, int dtype, int64_t T, int64_t H,
+                                      uint8_t* img, float* row_scale, hipStream_t s);
+hipError_t launch_rmsnorm_quantize_staged(const uint16_t* hid, const uint16_t* res,
+                                          const uint16_t* gamma, float eps, int64_t T, int64_t H,
+                                          int64_t Hu, uint16_t* res_out, uint8_t* img,
+                                          float* row_scale, hipStream_t s);
+hipError_t launch_project_staged(const uint8_t* img, const float* row_scale,
+                                 const uint8_t* w_packed, const float* chan_scale,
+                                 const uint16_t* bias, int64_t T, int64_t H, int64_t I, int64_t Iq,
+                                 int64_t Ik, int64_t d, bool nbsd, uint16_t* out, float* ssq,
+                                 uint8_t* ws, hipStream_t s);
 hipError_t launch_project(const uint8_t* a_codes, int64_t a_stride, const uint8_t* a_scales,
                           int64_t s_stride, const uint8_t* w_packed, const float* chan_scale,
                           const uint16_t* bias, int64_t T, int64_t H, int64_t I, int64_t Iq,

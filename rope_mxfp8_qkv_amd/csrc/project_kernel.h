@@ -845,6 +845,12 @@ __global__ void __launch_bounds__(256) act_repack_kernel(const uint8_t* __restri
   reinterpret_cast<uint4*>(img)[(tm * KS + t) * (kStageImage / 16) + p] = o;
 }
 
+// Zeroes the per-XCD tile counters (for launches without an activation repack, which
+// otherwise does it).
+__global__ void __launch_bounds__(64) reset_counters_kernel(unsigned* __restrict__ ctr) {
+  if (threadIdx.x < kXcds) ctr[threadIdx.x] = 0;
+}
+
 // MX activation exponents [T, stride] -> per (token tile tm, superstep s) [256 tokens][2]
 // dwords: byte q of dword g of token r = exponent of K-block 8 s + 2 q + g of row 256 tm + r,
 // 127 (2^0) past T or H (whose codes are zero).  One thread per (token, dword).

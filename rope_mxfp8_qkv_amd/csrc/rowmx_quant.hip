@@ -65,15 +65,41 @@ __device__ __forceinline__ void unpack8(const uint4 v, float* f) {
 // instruction of a wavefront covers 1 KiB contiguous.
 __device__ __forceinline__ int64_t chunk_of(int k) { return threadIdx.x + (int64_t)k * blockDim.x; }
 
+// Destinations of an encoded ROW_MX row.
+// PackedRow: the pages' packed row, H codes then the fp32 scale (4-byte tail at byte H).
+struct PackedRow {
+  uint8_t* row;
+  int64_t H;
+  __device__ uint8_t* chunk(int64_t c) const { return row + c * kChunk; }
+  __device__ void scale(float s) const { *reinterpret_cast<float*>(row + H) = s; }
+  __device__ int64_t pad_chunks() const { return 0; }
+};
+// StagedRow: the projection's stage-image layout.  Codes of row m, K-byte h go to image offset
+// ((m / 256 * KS + h / 64) * 256 + m % 256) * 64 + (((h / 16) % 4 ^ stage_swizzle(m % 256)) << 4)
+// + h % 16 (the layout its K-loop DMA-copies into LDS unchanged); K-bytes from H up to KS * 64
+// are written as zero codes; the scale goes to a separate fp32 array.
+struct StagedRow {
+  uint8_t* base;      // image + (m / 256 * KS) * kStageImage + (m % 256) * kStage
+  int swz;            // stage_swizzle(m % 256)
+  float* scale_p;     // &row_scale[m]
+  int64_t padded;     // KS * 64 / kChunk chunks per row in the image
+  __device__ uint8_t* chunk(int64_t c) const {
+    return base + (c >> 3) * kStageImage + ((((int)(c >> 1) & 3) ^ swz) << 4) + (c & 1) * kChunk;
+  }
+  __device__ void scale(float s) const { *scale_p = s; }
+  __device__ int64_t pad_chunks() const { return padded; }
+};
+
 // s = fl32(amax / 448) (IEEE division); codes = E4M3 RNE saturating of fl32(y / s); a zero row
-// stores s = 0 and zero codes; thread 0 writes the scale tail.
+// stores s = 0 and zero codes; thread 0 writes the scale.
 // fl32(y / s) is formed as fl32(fl64(y * fl64(1 / s))): the fp64 product is within 2^-52 of
 // y / s, while a quotient of two fp32 numbers never is an fp32 rounding midpoint and lies at
 // least 2^-49 (relative) away from every one, so rounding the product to fp32 gives exactly the
 // IEEE quotient for every normal result (results below 2^-126 encode to a signed zero code
 // either way).  One fp64 divide per thread replaces an fp32 divide per element.
+template <typename Dst>
 __device__ __forceinline__ void encode_store(const float (&y)[kCpt][kChunk], float amax,
-                                             int64_t H, uint8_t* __restrict__ row_out) {
+                                             int64_t H, const Dst& dst) {
   const float s = amax / 448.0f;
   const double rinv = 1.0 / (double)s;
   const int64_t nchunks = H / kChunk;
@@ -89,17 +115,42 @@ __device__ __forceinline__ void encode_store(const float (&y)[kCpt][kChunk], flo
         for (int e = 0; e < 4; ++e)
           hi |= f32_to_e4m3((float)((double)y[k][4 + e] * rinv)) << (8 * e);
       }
-      *reinterpret_cast<u32x2_a4*>(row_out + c * kChunk) = u32x2_a4{lo, hi};
+      *reinterpret_cast<u32x2_a4*>(dst.chunk(c)) = u32x2_a4{lo, hi};
+    } else if (c < dst.pad_chunks()) {
+      *reinterpret_cast<u32x2_a4*>(dst.chunk(c)) = u32x2_a4{0u, 0u};
     }
   }
-  if (threadIdx.x == 0) *reinterpret_cast<float*>(row_out + H) = s;
+  if (threadIdx.x == 0) dst.scale(s);
 }
 
-template <bool BF16>
-__global__ void __launch_bounds__(1024) row_quantize_kernel(const void* __restrict__ x, int64_t H,
-                                                             uint8_t* __restrict__ packed) {
+// The staged destination of row m (KS K-stages per row).
+__device__ __forceinline__ StagedRow staged_row(uint8_t* img, float* row_scale, int64_t m, int KS) {
+  const int r = (int)(m & (kTileM - 1));
+  return StagedRow{img + (m / kTileM) * KS * (int64_t)kStageImage + (int64_t)r * kStage,
+                   stage_swizzle(r), row_scale + m, (int64_t)KS * kStage / kChunk};
+}
+
+// Rows from T up to the end of the last 256-row tile of a staged image: zero codes (the
+// projection multiplies them but never stores their outputs).  One block per row.
+__device__ __forceinline__ void staged_zero_row(uint8_t* img, int64_t m, int KS) {
+  const StagedRow d = staged_row(img, nullptr, m, KS);
+  for (int64_t c = threadIdx.x; c < d.padded; c += blockDim.x)
+    *reinterpret_cast<u32x2_a4*>(d.chunk(c)) = u32x2_a4{0u, 0u};
+}
+
+// y = x (fp32 or bf16 rows), ROW_MX encoded into packed rows [T, H + 4] or, with STAGED, into
+// the stage-image layout plus fp32 row scales (grid: T rows, rounded up to whole 256-row tiles).
+template <bool BF16, bool STAGED>
+__global__ void __launch_bounds__(1024) row_quantize_kernel(const void* __restrict__ x, int64_t T,
+                                                             int64_t H, uint8_t* __restrict__ out,
+                                                             float* __restrict__ row_scale,
+                                                             int KS) {
   __shared__ float sh[kMaxWaves];
   const int64_t row = blockIdx.x;
+  if (STAGED && row >= T) {
+    staged_zero_row(out, row, KS);
+    return;
+  }
   const int64_t nchunks = H / kChunk;
   float y[kCpt][kChunk];
   float amax = 0.0f;
@@ -124,7 +175,10 @@ __global__ void __launch_bounds__(1024) row_quantize_kernel(const void* __restri
     }
   }
   amax = block_max(amax, sh);
-  encode_store(y, amax, H, packed + row * (H + 4));
+  if (STAGED)
+    encode_store(y, amax, H, staged_row(out, row_scale, row, KS));
+  else
+    encode_store(y, amax, H, PackedRow{out + row * (H + 4), H});
 }
 
 // Steps 1-4 of the fused producer for one row, into registers y (zeros past H):
@@ -183,14 +237,19 @@ __device__ __forceinline__ void normed_row(const uint16_t* __restrict__ hid,
   }
 }
 
-template <bool RES>
+template <bool RES, bool STAGED>
 __global__ void __launch_bounds__(1024) rmsnorm_quantize_kernel(
     const uint16_t* __restrict__ hid, const uint16_t* __restrict__ res,
-    const uint16_t* __restrict__ gamma, float eps, int64_t H, int64_t Hu,
-    uint16_t* __restrict__ res_out, uint8_t* __restrict__ packed) {
+    const uint16_t* __restrict__ gamma, float eps, int64_t T, int64_t H, int64_t Hu,
+    uint16_t* __restrict__ res_out, uint8_t* __restrict__ out, float* __restrict__ row_scale,
+    int KS) {
   __shared__ double shd[kMaxWaves];
   __shared__ float shf[kMaxWaves];
   const int64_t row = blockIdx.x;
+  if (STAGED && row >= T) {
+    staged_zero_row(out, row, KS);
+    return;
+  }
   float y[kCpt][kChunk];
   normed_row<RES>(hid, res, gamma, eps, H, Hu, res_out, row, y, shd);
   float amax = 0.0f;
@@ -199,7 +258,10 @@ __global__ void __launch_bounds__(1024) rmsnorm_quantize_kernel(
 #pragma unroll
     for (int e = 0; e < kChunk; ++e) amax = fmaxf(amax, fabsf(y[k][e]));
   amax = block_max(amax, shf);
-  encode_store(y, amax, H, packed + row * (H + 4));
+  if (STAGED)
+    encode_store(y, amax, H, staged_row(out, row_scale, row, KS));
+  else
+    encode_store(y, amax, H, PackedRow{out + row * (H + 4), H});
 }
 
 // MX block-32 encoding of y (the 4 consecutive chunks of a 32-element block belong to 4
@@ -312,9 +374,24 @@ hipError_t launch_row_quantize(const void* x, int dtype, int64_t T, int64_t H, u
                                hipStream_t s) {
   const dim3 grid((unsigned)T), block(block_threads(H));
   if (dtype == 1)
-    hipLaunchKernelGGL(row_quantize_kernel<true>, grid, block, 0, s, x, H, packed);
+    hipLaunchKernelGGL((row_quantize_kernel<true, false>), grid, block, 0, s, x, T, H, packed,
+                       nullptr, 0);
   else
-    hipLaunchKernelGGL(row_quantize_kernel<false>, grid, block, 0, s, x, H, packed);
+    hipLaunchKernelGGL((row_quantize_kernel<false, false>), grid, block, 0, s, x, T, H, packed,
+                       nullptr, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_quantize_staged(const void* x, int dtype, int64_t T, int64_t H,
+                                      uint8_t* img, float* row_scale, hipStream_t s) {
+  const dim3 grid((unsigned)(ceil_div(T, kTileM) * kTileM)), block(block_threads(H));
+  const int KS = (int)packed_stages(H);
+  if (dtype == 1)
+    hipLaunchKernelGGL((row_quantize_kernel<true, true>), grid, block, 0, s, x, T, H, img,
+                       row_scale, KS);
+  else
+    hipLaunchKernelGGL((row_quantize_kernel<false, true>), grid, block, 0, s, x, T, H, img,
+                       row_scale, KS);
   return hipGetLastError();
 }
 
@@ -323,11 +400,26 @@ hipError_t launch_rmsnorm_quantize(const uint16_t* hid, const uint16_t* res, con
                                    uint8_t* packed, hipStream_t s) {
   const dim3 grid((unsigned)T), block(block_threads(H));
   if (res)
-    hipLaunchKernelGGL(rmsnorm_quantize_kernel<true>, grid, block, 0, s, hid, res, gamma, eps, H,
-                       Hu, res_out, packed);
+    hipLaunchKernelGGL((rmsnorm_quantize_kernel<true, false>), grid, block, 0, s, hid, res,
+                       gamma, eps, T, H, Hu, res_out, packed, nullptr, 0);
   else
-    hipLaunchKernelGGL(rmsnorm_quantize_kernel<false>, grid, block, 0, s, hid, res, gamma, eps,
-                       H, Hu, res_out, packed);
+    hipLaunchKernelGGL((rmsnorm_quantize_kernel<false, false>), grid, block, 0, s, hid, res,
+                       gamma, eps, T, H, Hu, res_out, packed, nullptr, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_quantize_staged(const uint16_t* hid, const uint16_t* res,
+                                          const uint16_t* gamma, float eps, int64_t T, int64_t H,
+                                          int64_t Hu, uint16_t* res_out, uint8_t* img,
+                                          float* row_scale, hipStream_t s) {
+  const dim3 grid((unsigned)(ceil_div(T, kTileM) * kTileM)), block(block_threads(H));
+  const int KS = (int)packed_stages(H);
+  if (res)
+    hipLaunchKernelGGL((rmsnorm_quantize_kernel<true, true>), grid, block, 0, s, hid, res,
+                       gamma, eps, T, H, Hu, res_out, img, row_scale, KS);
+  else
+    hipLaunchKernelGGL((rmsnorm_quantize_kernel<false, true>), grid, block, 0, s, hid, res,
+                       gamma, eps, T, H, Hu, res_out, img, row_scale, KS);
   return hipGetLastError();
 }
 

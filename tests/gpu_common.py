@@ -140,3 +140,23 @@ def flags_of(p: synth.Projection) -> int:
 def custom_projection(name, T, H, nq, nkv, d, rope="1d", seed=99):
     return synth.Projection(name, seed, T=T, H=H, num_heads=nq, num_kv_heads=nkv, head_dim=d,
                             rope=rope, norm_q=True, norm_k=nkv > 0)
+
+
+def staged_index(rows: np.ndarray, H: int) -> np.ndarray:
+    """Byte offsets, in the staged activation image, of the codes of `rows` (elements 0..H-1):
+    row t, element h at ((t / 256 * KS + h / 64) * 256 + t % 256) * 64
+    + ((((h / 16) % 4) ^ sw(t % 256)) << 4) + h % 16, KS = 4 ceil(H / 256),
+    sw(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1) (the layout include/qkvmx.h states)."""
+    KS = 4 * -(-H // 256)
+    t = np.asarray(rows, dtype=np.int64)[:, None]
+    h = np.arange(H, dtype=np.int64)[None, :]
+    r = t % 256
+    sw = ((r >> 1) & 3) ^ ((r >> 3) & 1)
+    return (((t // 256) * KS + h // 64) * 256 + r) * 64 + ((((h // 16) % 4) ^ sw) << 4) + h % 16
+
+
+def unstage(image, rows: np.ndarray, H: int) -> np.ndarray:
+    """Codes [len(rows), H] gathered from a device image (gather on the device)."""
+    import torch
+    idx = torch.as_tensor(staged_index(rows, H).reshape(-1), device=image.device)
+    return image[idx].reshape(len(rows), H).cpu().numpy()

@@ -52,6 +52,13 @@ def test_size_queries():
     assert L.qkvmx_workspace_bytes(75600, 5120, 15360) == 296 * 80 * 16384 + 120 * 75600 * 8 + 256
     assert L.qkvmx_workspace_bytes(0, 256, 16) == 0
     assert L.qkvmx_workspace_bytes(4, 100, 16) == 0
+    # staged activations: the image alone (whole 256-row tiles x KS stages x 16 KiB); the staged
+    # projection's workspace holds only the partials and the counter block
+    assert L.qkv_act_image_bytes(75600, 5120) == 296 * 80 * 16384
+    assert L.qkv_act_image_bytes(300, 2080) == 2 * 36 * 16384
+    assert L.qkv_act_image_bytes(4, 100) == 0
+    assert L.qkv_staged_workspace_bytes(75600, 15360) == 120 * 75600 * 8 + 256
+    assert L.qkv_staged_workspace_bytes(0, 16) == 0
 
 
 P = 0x10000   # a fake, well-aligned device address: validation fails before it is used
@@ -135,6 +142,43 @@ def test_producer_and_weight_validation():
     assert L.mx_weight_quantize(P, 100, 16, P, P, None) == 2
     assert L.qkv_weight_prepack(P, P, 256, 16, P, 10, None) == 2                 # buffer too small
     assert L.qkv_weight_prepack(P, P, 256, 16, P + 64, 1 << 20, None) == 3
+
+
+def _stproj(L, **kw):
+    a = dict(act_image=P, image_bytes=1 << 30, row_scale=P, w_packed=P, w_channel_scale=None,
+             bias=None, T=4, H=256, num_heads=2, num_kv_heads=2, head_dim=64, layout=0, out=P,
+             ssq=None, workspace=P, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return L.qkv_rowmx_project_staged(*a.values())
+
+
+def test_staged_path_validation():
+    L = _lib()
+    assert _stproj(L, act_image=None) == 1
+    assert _stproj(L, row_scale=None) == 1
+    assert _stproj(L, H=100) == 2
+    assert _stproj(L, image_bytes=16384 * 4 - 1) == 2              # image too small for H = 256
+    assert _stproj(L, head_dim=40) == 2
+    assert _stproj(L, layout=2) == 4
+    assert _stproj(L, workspace=None) == 5
+    assert _stproj(L, ws_bytes=8) == 5
+    assert _stproj(L, act_image=P + 16) == 3
+    assert _stproj(L, row_scale=P + 2) == 3
+    assert _stproj(L, out=P + 2) == 3
+    # producers: (x, dtype, T, H, image, image_bytes, row_scale, stream)
+    assert L.row_quantize_staged(P, 0, 4, 256, P, 1 << 20, None, None) == 1
+    assert L.row_quantize_staged(P, 3, 4, 256, P, 1 << 20, P, None) == 4
+    assert L.row_quantize_staged(P, 0, 4, 250, P, 1 << 20, P, None) == 2
+    assert L.row_quantize_staged(P, 0, 4, 256, P, 100, P, None) == 2
+    assert L.row_quantize_staged(P, 0, 4, 32768, P, 1 << 30, P, None) == 6
+    assert L.row_quantize_staged(P, 0, 4, 256, P + 8, 1 << 20, P, None) == 3
+    # (hidden, residual, gamma, eps, T, H, Hu, residual_out, image, image_bytes, row_scale, s)
+    assert L.rmsnorm_mx_quantize_staged(P, P, P, 1e-6, 4, 256, 0, None, P, 1 << 20, P, None) == 4
+    assert L.rmsnorm_mx_quantize_staged(P, None, P, 1e-6, 4, 256, 300, None, P, 1 << 20, P, None) == 2
+    assert L.rmsnorm_mx_quantize_staged(P, None, P, -1.0, 4, 256, 0, None, P, 1 << 20, P, None) == 4
+    assert L.rmsnorm_mx_quantize_staged(P, None, P, 1e-6, 4, 256, 0, None, P, 10, P, None) == 2
+    assert L.rmsnorm_mx_quantize_staged(P, None, P, 1e-6, 4, 256, 0, None, P, 1 << 20, P + 2, None) == 3
+    assert L.rmsnorm_mx_quantize_staged(None, None, P, 1e-6, 4, 256, 0, None, P, 1 << 20, P, None) == 1
 
 
 def _mxproj(L, **kw):

@@ -50,6 +50,17 @@ class Gpu:
                                  bias=G.bf16_dev(bias, self.dev), ssq=ssq, workspace=ws)
         return out, ssq
 
+    def project_staged(self, p, img, sc, wp, bias):
+        import torch
+        out = torch.empty((p.T, p.I), dtype=torch.bfloat16, device=self.dev)
+        ssq = torch.empty((p.T, 2), dtype=torch.float32, device=self.dev)
+        ws = torch.empty(self.q.qkv_staged_workspace_bytes(p.T, p.I), dtype=torch.uint8,
+                         device=self.dev)
+        self.q.qkv_rowmx_project_staged(img, sc, wp, out, H=p.H, num_heads=p.num_heads,
+                                        num_kv_heads=p.num_kv_heads, head_dim=p.head_dim,
+                                        bias=G.bf16_dev(bias, self.dev), ssq=ssq, workspace=ws)
+        return out, ssq
+
     def pass2(self, p, out, ssq, gq, gk, cos, sin):
         fl = G.flags_of(p)
         if fl == 0:
@@ -96,7 +107,7 @@ def _idx(rows, device):
     return torch.as_tensor(np.asarray(rows, dtype=np.int64), device=device)
 
 
-def _run_self_attention(p, producer: bool):
+def _run_self_attention(p, producer: bool, staged: bool = False):
     import torch
     q = __import__("rope_mxfp8_qkv_amd")
     q.lib()
@@ -104,21 +115,38 @@ def _run_self_attention(p, producer: bool):
     gpu = Gpu(q, dev)
     rows = sample_rows(p.T)
     print(f"[fullsize] {p.name}: T={p.T} H={p.H} I={p.I} rows={len(rows)}", flush=True)
-    packed = torch.empty((p.T, p.H + 4), dtype=torch.uint8, device=dev)
+    if staged:
+        img = torch.empty(q.qkv_act_image_bytes(p.T, p.H), dtype=torch.uint8, device=dev)
+        sc = torch.empty((p.T,), dtype=torch.float32, device=dev)
+    else:
+        packed = torch.empty((p.T, p.H + 4), dtype=torch.uint8, device=dev)
     if producer:
         hid, res, gam = synth.producer_inputs(p.seed_id, p.T, p.H)
         res_out = torch.empty((p.T, p.H), dtype=torch.bfloat16, device=dev)
-        q.rmsnorm_mx_quantize(G.bf16_dev(hid, dev), G.bf16_dev(gam, dev), 1e-6, packed,
-                              residual=G.bf16_dev(res, dev), residual_out=res_out)
+        if staged:
+            q.rmsnorm_mx_quantize_staged(G.bf16_dev(hid, dev), G.bf16_dev(gam, dev), 1e-6, img, sc,
+                                         residual=G.bf16_dev(res, dev), residual_out=res_out)
+        else:
+            q.rmsnorm_mx_quantize(G.bf16_dev(hid, dev), G.bf16_dev(gam, dev), 1e-6, packed,
+                                  residual=G.bf16_dev(res, dev), residual_out=res_out)
         r_ref, packed_ref, _ = oracle.rmsnorm_rowmx(hid[rows], res[rows], gam, 1e-6)
         G.check_equal(G.bf16_host(res_out[_idx(rows, dev)]), r_ref, "residual_out rows")
         del hid, res, res_out
     else:
         x = synth.activation(p)
-        q.row_quantize_packed(G.to_dev(x, dev), packed)
+        if staged:
+            q.row_quantize_staged(G.to_dev(x, dev), img, sc)
+        else:
+            q.row_quantize_packed(G.to_dev(x, dev), packed)
         packed_ref = oracle.rowmx_quantize(x[rows])
         del x
-    G.check_equal(packed[_idx(rows, dev)].cpu().numpy(), packed_ref, "ROW_MX rows")
+    if staged:
+        codes_ref, s_ref = oracle.rowmx_unpack(packed_ref, p.H)
+        G.check_equal(G.unstage(img, rows, p.H), codes_ref, "staged code rows")
+        G.check_equal(sc[_idx(rows, dev)].cpu().numpy().view(np.uint32),
+                      s_ref.astype(np.float32).view(np.uint32), "row scales")
+    else:
+        G.check_equal(packed[_idx(rows, dev)].cpu().numpy(), packed_ref, "ROW_MX rows")
     w = synth.weight(p)
     codes, e8, wp = gpu.weight(w)
     w_codes, w_e8 = oracle.mx_weight_quantize(w)
@@ -126,7 +154,10 @@ def _run_self_attention(p, producer: bool):
     G.check_equal(codes.cpu().numpy(), w_codes, "weight codes")
     bias, gq, gk = synth.bias_bf16(p), synth.gamma_bf16(p, "q"), synth.gamma_bf16(p, "k")
     cos, sin = synth.rope_tables(p)
-    out, ssq = gpu.project(p, packed, wp, bias)
+    if staged:
+        out, ssq = gpu.project_staged(p, img, sc, wp, bias)
+    else:
+        out, ssq = gpu.project(p, packed, wp, bias)
     seg = (p.num_heads + p.num_kv_heads) * p.head_dim
     ti = _idx(rows, dev)
     v_before = out[ti, seg:].clone()
@@ -144,6 +175,12 @@ def test_fullsize_self_attention_video():
 def test_fullsize_producer_then_self_attention():
     """bf16 hidden + residual -> fused producer -> projection -> norm + 3-axis RoPE."""
     _run_self_attention(synth.CONFIGS[5].calls[0], producer=True)
+
+
+def test_fullsize_staged_producer_then_self_attention():
+    """The benchmark's default step: fused producer writing staged codes and row scales ->
+    staged projection -> norm + 3-axis RoPE."""
+    _run_self_attention(synth.CONFIGS[5].calls[0], producer=True, staged=True)
 
 
 def test_fullsize_mx_producer_then_self_attention():

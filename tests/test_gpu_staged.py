@@ -1,0 +1,171 @@
+"""GPU parity of the staged ROW_MX path: producers that write the codes in the projection's
+stage-image layout (plus fp32 row scales) and the projection that consumes them without a
+per-call re-layout.
+
+Codes and scales are compared bit for bit with the oracle's ROW_MX rows (the image is read back
+through the layout formula of include/qkvmx.h, restated in gpu_common.staged_index); the padding
+of the image (K past H, rows past T in the last 256-row tile) must hold zero codes.  The staged
+projection must give the same bytes as the packed-row projection on the same codes and scales,
+and both are checked against the oracle.
+"""
+import numpy as np
+import pytest
+
+import gpu_common as G
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import rope_mxfp8_qkv_amd as q
+    q.lib()
+    return q
+
+
+def _image(q, T, H, dev):
+    import torch
+    return torch.full((q.qkv_act_image_bytes(T, H),), 0xA5, dtype=torch.uint8, device=dev)
+
+
+def _check_padding(img, T, H):
+    """Every image byte outside the T x H codes is zero."""
+    n = img.numel()
+    used = np.zeros(n, dtype=bool)
+    used[G.staged_index(np.arange(T), H).reshape(-1)] = True
+    host = img.cpu().numpy()
+    assert not host[~used].any(), f"{int((host[~used] != 0).sum())} padding bytes are not zero"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_row_quantize_staged_bit_exact(dtype):
+    import torch
+    q = _lib()
+    dev = G.torch_dev()
+    rng = np.random.default_rng(17)
+    T, H = 300, 2080                      # ragged last tile; K padding (2080 = 8 x 256 + 32)
+    x = (rng.standard_normal((T, H)) * rng.uniform(1e-3, 1e3, (T, 1))).astype(np.float32)
+    x[4] = 0.0
+    x[5, :7] = -0.0
+    x[6, 3] = -1e-30
+    if dtype == "bf16":
+        bits = synth.to_bf16_bits(x)
+        x = synth.bf16_bits_to_f32(bits)
+        xd = G.bf16_dev(bits, dev)
+    else:
+        xd = G.to_dev(x, dev)
+    codes_ref, s_ref = oracle.rowmx_unpack(oracle.rowmx_quantize(x), H)
+    img = _image(q, T, H, dev)
+    sc = torch.full((T,), float("nan"), dtype=torch.float32, device=dev)
+    q.row_quantize_staged(xd, img, sc)
+    torch.cuda.synchronize()
+    G.check_equal(G.unstage(img, np.arange(T), H), codes_ref, "staged codes")
+    G.check_equal(sc.cpu().numpy().view(np.uint32), s_ref.astype(np.float32).view(np.uint32),
+                  "row scales")
+    _check_padding(img, T, H)
+
+
+@pytest.mark.parametrize("with_res,Hu", [(True, 0), (False, 0), (True, 4000)])
+def test_rmsnorm_quantize_staged_bit_exact(with_res, Hu):
+    import torch
+    q = _lib()
+    dev = G.torch_dev()
+    T, H = 300, 5120
+    hid, res, gam = synth.producer_inputs(77, T, H)
+    if Hu:
+        hid[:, Hu:] = 0
+        res[:, Hu:] = 0
+    res_ref, packed_ref, _ = oracle.rmsnorm_rowmx(hid, res if with_res else None, gam, 1e-6, Hu)
+    codes_ref, s_ref = oracle.rowmx_unpack(packed_ref, H)
+    img = _image(q, T, H, dev)
+    sc = torch.full((T,), float("nan"), dtype=torch.float32, device=dev)
+    res_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if with_res else None
+    q.rmsnorm_mx_quantize_staged(G.bf16_dev(hid, dev), G.bf16_dev(gam, dev), 1e-6, img, sc,
+                                 residual=G.bf16_dev(res, dev) if with_res else None,
+                                 residual_out=res_out, unpadded_h=Hu)
+    torch.cuda.synchronize()
+    if with_res:
+        G.check_equal(G.bf16_host(res_out), res_ref, "residual_out")
+    G.check_equal(G.unstage(img, np.arange(T), H), codes_ref, "staged codes")
+    G.check_equal(sc.cpu().numpy().view(np.uint32), s_ref.astype(np.float32).view(np.uint32),
+                  "row scales")
+    _check_padding(img, T, H)
+
+
+STAGED_CASES = [
+    ("C1", synth.CONFIGS[1].calls[0], 0),
+    ("T1", G.custom_projection("t1", T=1, H=256, nq=2, nkv=2, d=64), 0),
+    ("gqa-ragged", G.custom_projection("gqa", T=129, H=96, nq=4, nkv=2, d=64), 0),
+    ("ragged-N-nbsd", G.custom_projection("rn", T=300, H=512, nq=3, nkv=1, d=128), 1),
+    ("single-seg", G.custom_projection("ss", T=257, H=1024, nq=5, nkv=0, d=128, rope=None), 0),
+]
+
+
+@pytest.mark.parametrize("name,p,layout", STAGED_CASES, ids=[c[0] for c in STAGED_CASES])
+def test_projection_staged_parity(name, p, layout):
+    """Staged producer -> staged projection == packed producer -> packed projection (bytes),
+    and both within tolerance of the oracle."""
+    import torch
+    q = _lib()
+    dev = G.torch_dev()
+    inp = G.make_inputs(p)
+    codes, sA = oracle.rowmx_unpack(inp.packed, p.H)
+    X, ssq_ref = oracle.project(codes, sA, inp.w_codes, inp.w_e8m0, None, inp.bias,
+                                num_heads=p.num_heads, num_kv_heads=p.num_kv_heads,
+                                head_dim=p.head_dim)
+    wp = q.prepare_weight(G.to_dev(inp.w_codes, dev), G.to_dev(inp.w_e8m0, dev), p.H, p.I)
+    shape = (p.I // p.head_dim, p.T, p.head_dim) if layout else (p.T, p.I)
+    bias = G.bf16_dev(inp.bias, dev)
+    xd = G.to_dev(inp.x, dev)
+    # packed rows
+    packed = torch.empty((p.T, p.H + 4), dtype=torch.uint8, device=dev)
+    q.row_quantize_packed(xd, packed)
+    out_p = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    ssq_p = torch.full((p.T, 2), float("nan"), dtype=torch.float32, device=dev)
+    ws_p = torch.empty(q.qkvmx_workspace_bytes(p.T, p.H, p.I), dtype=torch.uint8, device=dev)
+    q.qkv_rowmx_project(packed, wp, out_p, H=p.H, num_heads=p.num_heads,
+                        num_kv_heads=p.num_kv_heads, head_dim=p.head_dim, bias=bias, ssq=ssq_p,
+                        workspace=ws_p, layout=layout)
+    # staged
+    img = _image(q, p.T, p.H, dev)
+    sc = torch.empty((p.T,), dtype=torch.float32, device=dev)
+    q.row_quantize_staged(xd, img, sc)
+    out_s = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    ssq_s = torch.full((p.T, 2), float("nan"), dtype=torch.float32, device=dev)
+    ws_s = torch.empty(q.qkv_staged_workspace_bytes(p.T, p.I), dtype=torch.uint8, device=dev)
+    q.qkv_rowmx_project_staged(img, sc, wp, out_s, H=p.H, num_heads=p.num_heads,
+                               num_kv_heads=p.num_kv_heads, head_dim=p.head_dim, bias=bias,
+                               ssq=ssq_s, workspace=ws_s, layout=layout)
+    torch.cuda.synchronize()
+    assert torch.equal(out_s.view(torch.int16), out_p.view(torch.int16)), f"{name}: outputs differ"
+    assert torch.equal(ssq_s, ssq_p), f"{name}: sums differ"
+    got = G.bf16_host(out_s)
+    if layout:
+        got = oracle.nbsd_to_bsd(got)
+    G.check_close(got, X, f"{name} X")
+    G.check_ssq(ssq_s.cpu().numpy(), ssq_ref, f"{name} ssq")
+
+
+def test_projection_staged_repeated_calls_share_workspace():
+    """Two calls in a row on one workspace (the tile counters are reset by each call), the
+    second with fewer tokens."""
+    import torch
+    q = _lib()
+    dev = G.torch_dev()
+    p = G.custom_projection("rep", T=700, H=512, nq=2, nkv=2, d=128)
+    inp = G.make_inputs(p)
+    wp = q.prepare_weight(G.to_dev(inp.w_codes, dev), G.to_dev(inp.w_e8m0, dev), p.H, p.I)
+    ws = torch.empty(q.qkv_staged_workspace_bytes(p.T, p.I), dtype=torch.uint8, device=dev)
+    codes, sA = oracle.rowmx_unpack(inp.packed, p.H)
+    for T in (p.T, 300):
+        img = _image(q, T, p.H, dev)
+        sc = torch.empty((T,), dtype=torch.float32, device=dev)
+        q.row_quantize_staged(G.to_dev(inp.x[:T], dev), img, sc)
+        out = torch.full((T, p.I), float("nan"), dtype=torch.bfloat16, device=dev)
+        q.qkv_rowmx_project_staged(img, sc, wp, out, H=p.H, num_heads=2, num_kv_heads=2,
+                                   head_dim=128, bias=G.bf16_dev(inp.bias, dev), workspace=ws)
+        torch.cuda.synchronize()
+        X, _ = oracle.project(codes[:T], sA[:T], inp.w_codes, inp.w_e8m0, None, inp.bias,
+                              num_heads=2, num_kv_heads=2, head_dim=128)
+        G.check_close(G.bf16_host(out), X, f"T={T} X")
