@@ -140,6 +140,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=5, choices=[2, 3, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the MFMA-rate and copy-bandwidth calibration after the timed steps")
     ap.add_argument("--layout", choices=["bsd", "nbsd"], default="bsd",
                     help="output layout of the projection and pass 2 (BSD [T, I] or NBSd [I/d, T, d])")
     ap.add_argument("--act-layout", choices=["staged", "packed"], default="staged",
@@ -345,6 +347,55 @@ def run_gpu(args):
     return res
 
 
+def measure_ceilings():
+    """What this GPU sustains outside the kernels, measured in the same run (context for the
+    roofline fractions, which divide by the published peaks): the scaled FP8 MFMA issue rate on
+    register operands (random E4M3 codes, as the workload's, and zeros) with the clock the chip
+    held meanwhile, and the bandwidth of a plain device-to-device copy (read + write bytes)."""
+    import torch
+    import rope_mxfp8_qkv_amd as q
+    dev = torch.device("cuda:0")
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 20000
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    clocks = torch.empty((blocks, 2), dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for rnd in (True, False):
+        best = None
+        for _ in range(4):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            q.mfma_rate_probe(blocks, iters, rnd, sink, clocks)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b)
+            c = clocks.cpu().numpy().astype(np.float64)
+            ghz = float(np.mean(c[:, 0] / (c[:, 1] / 100e6)) / 1e9)
+            tf = blocks * 4 * iters * 16 * 131072.0 / (ms * 1e-3) / 1e12
+            if best is None or tf > best[0]:
+                best = (tf, ghz)
+        key = "random" if rnd else "zero"
+        res[f"mfma_{key}_operands_tflops"] = best[0]
+        res[f"mfma_{key}_operands_clock_ghz"] = best[1]
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    ts = []
+    for _ in range(6):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    res["hbm_copy_gbs"] = 2.0 * n / (float(np.median(ts[1:])) * 1e-3) / 1e9
+    res["mfma_probe"] = (f"{blocks} blocks x 4 wavefronts x {iters} x 16 "
+                         "V_MFMA_SCALE_F32_32X32X64_F8F6F4 on register operands, best of 4")
+    res["copy"] = f"torch device copy of {n} bytes, median of 5"
+    return res
+
+
 def cpu_baseline(cid, rows_n):
     """The oracle, as it stands, on the first ``rows_n`` tokens of the same workload."""
     import oracle
@@ -400,6 +451,14 @@ def main():
     r = run_gpu(args)
     p = r["p"]
     log(f"gpu: {r['ms_per_step']:.3f} ms/step, stages {r['stage_ms']}")
+    ceil = None if args.no_ceilings else measure_ceilings()
+    if ceil:
+        ceil["projection_frac_of_mfma_random"] = r["projection_tflops"] / ceil["mfma_random_operands_tflops"]
+        if r["norm_rope_gbs"]:
+            ceil["norm_rope_frac_of_copy"] = r["norm_rope_gbs"] / ceil["hbm_copy_gbs"]
+        if r["producer_gbs"]:
+            ceil["producer_frac_of_copy"] = r["producer_gbs"] / ceil["hbm_copy_gbs"]
+        log(f"ceilings: {ceil}")
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_rows} rows")
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.config, args.cpu_rows)
@@ -456,6 +515,7 @@ def main():
             "producer_gbs": r["producer_gbs"],
             "producer_hbm_frac": (r["producer_gbs"] / PEAK_HBM_GBS) if r["producer_gbs"] else None,
         },
+        "ceilings": ceil,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

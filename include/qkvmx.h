@@ -315,6 +315,21 @@ qkvmx_status qk_norm_rope_apply(uint16_t* qkv, const float* ssq, const uint16_t*
                                 int32_t num_kv_heads, int32_t head_dim, float eps,
                                 uint32_t flags, int32_t layout, hipStream_t stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Roofline calibration (a measurement helper, not a step of the method).
+ * ------------------------------------------------------------------------------------------ */
+
+/* Launches `blocks` blocks of 256 threads, each wavefront issuing iters x 16 scaled FP8 MFMAs
+ * (V_MFMA_SCALE_F32_32X32X64_F8F6F4, 2 * 32 * 32 * 64 flop each) on register operands: random
+ * E4M3 codes (random_operands != 0) or zeros; nothing else touches memory until the end.
+ *   sink    [blocks * 256] fp32, written (keeps the results live).
+ *   clocks  [blocks][2] uint64: elapsed core-clock cycles and 100 MHz reference ticks of the
+ *           loop, per block.
+ * flop = blocks * 4 * iters * 16 * 131072; the caller times the launch on `stream`.  Requires
+ * 1 <= blocks <= 65535, 1 <= iters <= 1 << 24; sink 4-byte, clocks 8-byte aligned. */
+qkvmx_status qkvmx_mfma_rate_probe(int32_t blocks, int32_t iters, int32_t random_operands,
+                                   float* sink, uint64_t* clocks, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ __all__ = [
     "qk_norm_rope_apply", "prepare_weight", "mx_block_quantize", "rmsnorm_mx_block_quantize",
     "qkv_mx_workspace_bytes", "qkv_mx_project", "qkv_rowmx_project_headnorm", "HEAD_RMS_NORM",
     "HEAD_LAYER_NORM", "qkv_act_image_bytes", "row_quantize_staged", "rmsnorm_mx_quantize_staged",
-    "qkv_staged_workspace_bytes", "qkv_rowmx_project_staged",
+    "qkv_staged_workspace_bytes", "qkv_rowmx_project_staged", "mfma_rate_probe",
 ]
 
 
@@ -245,3 +245,10 @@ def qk_norm_rope_apply(qkv, *, num_heads: int, num_kv_heads: int, head_dim: int,
     _check(lib().qk_norm_rope_apply(_ptr(qkv), _ptr(ssq), _ptr(q_gamma), _ptr(k_gamma), _ptr(cos),
                                     _ptr(sin), T, num_heads, num_kv_heads, head_dim, float(eps),
                                     flags, layout, _stream(stream)), "qk_norm_rope_apply")
+
+
+def mfma_rate_probe(blocks: int, iters: int, random_operands: bool, sink, clocks, stream=None):
+    """Roofline calibration: launches the MFMA issue-rate probe (see include/qkvmx.h);
+    ``sink`` fp32 [blocks * 256], ``clocks`` int64 [blocks, 2] (cycles, 100 MHz ticks)."""
+    _check(lib().qkvmx_mfma_rate_probe(blocks, iters, int(bool(random_operands)), _ptr(sink),
+                                       _ptr(clocks), _stream(stream)), "qkvmx_mfma_rate_probe")

@@ -136,6 +136,8 @@ hipError_t launch_mx_quantize(const void* x, int dtype, int64_t T, int64_t H, ui
 hipError_t launch_rmsnorm_mx(const uint16_t* hid, const uint16_t* res, const uint16_t* gamma,
                              float eps, int64_t T, int64_t H, int64_t Hu, uint16_t* res_out,
                              uint8_t* codes, uint8_t* e8, uint16_t* norm_out, hipStream_t s);
+hipError_t launch_mfma_rate(int blocks, int iters, bool random_operands, float* sink,
+                            uint64_t* clocks, hipStream_t s);
 hipError_t launch_norm_rope(uint16_t* qkv, const float* ssq, const uint16_t* q_gamma,
                             const uint16_t* k_gamma, const float* cos_tab, const float* sin_tab,
                             int64_t T, int nq, int nkv, int d, float eps, uint32_t flags,

@@ -391,4 +391,14 @@ qkvmx_status qk_norm_rope_apply(uint16_t* qkv, const float* ssq, const uint16_t*
                                      layout == QKVMX_LAYOUT_NBSD, stream), "qk_norm_rope_apply");
 }
 
+qkvmx_status qkvmx_mfma_rate_probe(int32_t blocks, int32_t iters, int32_t random_operands,
+                                   float* sink, uint64_t* clocks, hipStream_t stream) {
+  const char* fn = "qkvmx_mfma_rate_probe";
+  if (!sink || !clocks) return fail(QKVMX_ERR_NULL, "%s: null pointer", fn);
+  if (blocks < 1 || blocks > 65535 || iters < 1 || iters > (1 << 24))
+    return fail(QKVMX_ERR_SHAPE, "%s: need 1 <= blocks <= 65535, 1 <= iters <= 2^24", fn);
+  if (!aligned(sink, 4) || !aligned(clocks, 8)) return fail(QKVMX_ERR_ALIGN, "%s: sink 4-byte, clocks 8-byte aligned", fn);
+  return hip_status(launch_mfma_rate(blocks, iters, random_operands != 0, sink, clocks, stream), fn);
+}
+
 }  // extern "C"

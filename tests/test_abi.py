@@ -181,6 +181,14 @@ def test_staged_path_validation():
     assert L.rmsnorm_mx_quantize_staged(None, None, P, 1e-6, 4, 256, 0, None, P, 1 << 20, P, None) == 1
 
 
+def test_calibration_probe_validation():
+    L = _lib()
+    assert L.qkvmx_mfma_rate_probe(0, 10, 1, P, P, None) == 2
+    assert L.qkvmx_mfma_rate_probe(4, 0, 1, P, P, None) == 2
+    assert L.qkvmx_mfma_rate_probe(4, 10, 1, None, P, None) == 1
+    assert L.qkvmx_mfma_rate_probe(4, 10, 1, P, P + 4, None) == 3
+
+
 def _mxproj(L, **kw):
     a = dict(a_codes=P, a_row_stride=256, a_e8m0=P, a_e8m0_stride=8, w_packed=P,
              w_channel_scale=None, bias=None, T=4, H=256, num_heads=2, num_kv_heads=2,
