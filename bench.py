@@ -145,10 +145,11 @@ def parse():
     ap.add_argument("--layout", choices=["bsd", "nbsd"], default="bsd",
                     help="output layout of the projection and pass 2 (BSD [T, I] or NBSd [I/d, T, d])")
     ap.add_argument("--act-layout", choices=["staged", "packed"], default="staged",
-                    help="ROW_MX hand-over between producer and projection: codes written by the "
-                         "producer in the projection's stage-image layout with fp32 row scales "
-                         "(staged), or the pages' packed [T, H + 4] rows re-laid by the "
-                         "projection on every call (packed)")
+                    help="activation hand-over between producer and projection: codes (and MX "
+                         "exponents) written by the producer in the projection's operand layout, "
+                         "ROW_MX scales as an fp32 array (staged), or the pages' row layouts "
+                         "([T, H + 4] ROW_MX rows; [T, H] codes + [T, H / 32] exponents) re-laid "
+                         "by the projection on every call (packed)")
     ap.add_argument("--act", choices=["rowmx", "mx"], default="rowmx",
                     help="activation encoding: ROW_MX rows with an fp32 row scale (the projection's "
                          "packed_hidden) or MX block-32 (E8M0 exponent per 32 elements)")
@@ -240,13 +241,16 @@ def run_gpu(args):
         hgq, hgk = inp["gq"][:d].contiguous(), inp["gk"][:d].contiguous()
         hbq = (inp["bias"][:d].contiguous() if hn == q.HEAD_LAYER_NORM else None)
         hbk = (inp["bias"][d:2 * d].contiguous() if hn == q.HEAD_LAYER_NORM else None)
-    if mx:
+    if mx and args.act_layout == "packed":
         codes_a = torch.empty((T, H), dtype=torch.uint8, device=dev)
         e8_a = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
-    staged = not mx and not hn and args.act_layout == "staged"
+    staged = not hn and args.act_layout == "staged"
     if staged:
         img = torch.empty(q.qkv_act_image_bytes(T, H), dtype=torch.uint8, device=dev)
-        row_scale = torch.empty((T,), dtype=torch.float32, device=dev)
+        if mx:
+            eimg = torch.empty(q.qkv_act_exp_image_bytes(T, H) // 4, dtype=torch.int32, device=dev)
+        else:
+            row_scale = torch.empty((T,), dtype=torch.float32, device=dev)
     elif not mx:
         packed = torch.empty((T, H + 4), dtype=torch.uint8, device=dev)
     res_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if inp["producer"] else None
@@ -254,12 +258,14 @@ def run_gpu(args):
     out = (torch.empty((I // p.head_dim, T, p.head_dim), dtype=torch.bfloat16, device=dev)
            if args.layout == "nbsd" else torch.empty((T, I), dtype=torch.bfloat16, device=dev))
     ssq = torch.empty((T, 2), dtype=torch.float32, device=dev)
-    ws_n = (q.qkv_mx_workspace_bytes(T, H, I) if mx else
-            q.qkv_staged_workspace_bytes(T, I) if staged else q.qkvmx_workspace_bytes(T, H, I))
+    ws_n = (q.qkv_staged_workspace_bytes(T, I) if staged else
+            q.qkv_mx_workspace_bytes(T, H, I) if mx else q.qkvmx_workspace_bytes(T, H, I))
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
     flags = q.NORM_Q | q.NORM_K | q.FUSED_ROPE
     if not inp["producer"]:                         # activations fixed for the whole run
-        if mx:
+        if mx and staged:
+            q.mx_block_quantize_staged(inp["x"], img, eimg)
+        elif mx:
             q.mx_block_quantize(inp["x"], codes_a, e8_a)
         elif staged:
             q.row_quantize_staged(inp["x"], img, row_scale)
@@ -270,7 +276,10 @@ def run_gpu(args):
         if ev:
             ev[0].record(stream)
         if inp["producer"]:
-            if mx:
+            if mx and staged:
+                q.rmsnorm_mx_block_quantize_staged(inp["hid"], inp["pgamma"], 1e-6, img, eimg,
+                                                   residual=inp["res"], residual_out=res_out)
+            elif mx:
                 q.rmsnorm_mx_block_quantize(inp["hid"], inp["pgamma"], 1e-6, codes_a, e8_a,
                                             residual=inp["res"], residual_out=res_out)
             elif staged:
@@ -287,6 +296,10 @@ def run_gpu(args):
                                          norm_kind=hn, q_gamma=hgq, k_gamma=hgk, q_beta=hbq,
                                          k_beta=hbk, eps=1e-6, cos=inp["cos"], sin=inp["sin"],
                                          bias=inp["bias"], workspace=ws, layout=layout)
+        elif mx and staged:
+            q.qkv_mx_project_staged(img, eimg, wp, out, T=T, H=H, num_heads=p.num_heads,
+                                    num_kv_heads=p.num_kv_heads, head_dim=p.head_dim,
+                                    bias=inp["bias"], ssq=ssq, workspace=ws, layout=layout)
         elif staged:
             q.qkv_rowmx_project_staged(img, row_scale, wp, out, H=H, num_heads=p.num_heads,
                                        num_kv_heads=p.num_kv_heads, head_dim=p.head_dim,
@@ -482,16 +495,19 @@ def main():
                          if r["headnorm"] != "none" else
                          ("producer + QKV projection + across-heads norm + 3-axis RoPE"
                           if r["producer"] else "QKV projection + across-heads norm + RoPE"))
-                        + (", MX block-32 activations" if r["mx"] else
-                           ", ROW_MX activations staged in the projection's operand layout"
-                           if r["staged"] else ", ROW_MX activations as packed [T, H+4] rows"),
+                        + (", MX block-32 activations" if r["mx"] else ", ROW_MX activations")
+                        + (" staged in the projection's operand layout" if r["staged"] else
+                           " as natural-order codes and exponents" if r["mx"] else
+                           " as packed [T, H+4] rows"),
             "T": p.T, "H": p.H, "I": p.I, "num_heads": p.num_heads,
             "num_kv_heads": p.num_kv_heads, "head_dim": p.head_dim,
             "grid": list(p.grid) if p.grid else None, "layout": args.layout.upper().replace("NBSD", "NBSd"),
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": ("qkv_mx_project (activation repacks + project_kernel + ssq_reduce)"
+            "kernel": ("qkv_mx_project_staged (counter reset + project_kernel + ssq_reduce)"
+                       if r["mx"] and r["staged"] else
+                       "qkv_mx_project (activation repacks + project_kernel + ssq_reduce)"
                        if r["mx"] else
                        "qkv_rowmx_project_headnorm (activation repack + project_kernel)"
                        if r["headnorm"] != "none" else

@@ -179,6 +179,31 @@ qkvmx_status rmsnorm_mx_block_quantize(const uint16_t* hidden, const uint16_t* r
                                        uint8_t* codes_out, uint8_t* e8m0_out, uint16_t* norm_out,
                                        hipStream_t stream);
 
+/* Staged MX block-32 activations: the codes in the act_image layout of the staged ROW_MX
+ * producers, the exponents in the exponent image the projection's K-loop reads:
+ *   exp_image  [ceil(T / 256)][S][256][2] uint32, S = ceil(H / 256): byte q of dword g of row
+ *              t % 256 in superstep s of tile t / 256 is the E8M0 exponent of elements
+ *              [32 (8 s + 2 q + g), 32 (8 s + 2 q + g) + 32) of row t; 127 (2^0) for blocks
+ *              past H / 32 and for rows past T (whose codes are 0x00).
+ *              qkv_act_exp_image_bytes(T, H) bytes, 16-byte aligned.
+ * Codes and exponents are exactly those of mx_block_quantize / rmsnorm_mx_block_quantize. */
+size_t qkv_act_exp_image_bytes(int64_t T, int64_t H);
+
+/* mx_block_quantize with the staged outputs (act_image, exp_image above). */
+qkvmx_status mx_block_quantize_staged(const void* x, int32_t x_dtype, int64_t T, int64_t H,
+                                      uint8_t* act_image, size_t image_bytes, uint32_t* exp_image,
+                                      size_t exp_image_bytes, hipStream_t stream);
+
+/* rmsnorm_mx_block_quantize with the staged outputs (act_image, exp_image above); residual_out
+ * and norm_out as there. */
+qkvmx_status rmsnorm_mx_block_quantize_staged(const uint16_t* hidden, const uint16_t* residual,
+                                              const uint16_t* gamma, float eps, int64_t T,
+                                              int64_t H, int64_t unpadded_H,
+                                              uint16_t* residual_out, uint8_t* act_image,
+                                              size_t image_bytes, uint32_t* exp_image,
+                                              size_t exp_image_bytes, uint16_t* norm_out,
+                                              hipStream_t stream);
+
 /* ------------------------------------------------------------------------------------------
  * Pass 1: the projection ([QKV-CTE] "Upstream behavior", O[S, I] = A[S, H] @ W[H, I] + bias,
  * I = (num_heads + 2 * num_kv_heads) * head_dim; "Design 1)" step a).
@@ -288,6 +313,21 @@ qkvmx_status qkv_mx_project(const uint8_t* a_codes, int64_t a_row_stride, const 
                             int64_t H, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                             int32_t layout, uint16_t* out, float* ssq, void* workspace,
                             size_t ws_bytes, hipStream_t stream);
+
+/* qkv_mx_project on staged MX activations (act_image, exp_image written by
+ * mx_block_quantize_staged or rmsnorm_mx_block_quantize_staged for the same T and H): the same
+ * out and ssq, bit for bit, as qkv_mx_project on the natural-order codes and exponents.
+ *   act_image, exp_image   256-byte aligned, at least qkv_act_image_bytes(T, H) and
+ *                          qkv_act_exp_image_bytes(T, H) bytes.
+ *   workspace              >= qkv_staged_workspace_bytes(T, I) bytes, 256-byte aligned; scratch.
+ * Other arguments, layouts and errors as qkv_mx_project. */
+qkvmx_status qkv_mx_project_staged(const uint8_t* act_image, size_t image_bytes,
+                                   const uint32_t* exp_image, size_t exp_image_bytes,
+                                   const void* w_packed, const float* w_channel_scale,
+                                   const uint16_t* bias, int64_t T, int64_t H, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t layout,
+                                   uint16_t* out, float* ssq, void* workspace, size_t ws_bytes,
+                                   hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * Pass 2: across-heads RMSNorm + rotate-half RoPE, in place on Q and K; V is neither read nor

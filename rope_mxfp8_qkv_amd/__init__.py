@@ -24,6 +24,8 @@ __all__ = [
     "qkv_mx_workspace_bytes", "qkv_mx_project", "qkv_rowmx_project_headnorm", "HEAD_RMS_NORM",
     "HEAD_LAYER_NORM", "qkv_act_image_bytes", "row_quantize_staged", "rmsnorm_mx_quantize_staged",
     "qkv_staged_workspace_bytes", "qkv_rowmx_project_staged", "mfma_rate_probe",
+    "qkv_act_exp_image_bytes", "mx_block_quantize_staged", "rmsnorm_mx_block_quantize_staged",
+    "qkv_mx_project_staged",
 ]
 
 
@@ -147,6 +149,53 @@ def rmsnorm_mx_block_quantize(hidden, gamma, eps: float, codes_out, e8m0_out, re
                                            T, H, unpadded_h, _ptr(residual_out), _ptr(codes_out),
                                            _ptr(e8m0_out), _ptr(norm_out), _stream(stream)),
            "rmsnorm_mx_block_quantize")
+
+
+def qkv_act_exp_image_bytes(T: int, H: int) -> int:
+    """Bytes of the staged MX exponent image of T rows of H elements."""
+    return int(lib().qkv_act_exp_image_bytes(T, H))
+
+
+def mx_block_quantize_staged(x, act_image, exp_image, stream=None):
+    """x [T, H] fp32 or bf16 -> MX block-32 codes in the staged image layout and exponents in
+    the staged exponent image (uint8 / int32 tensors of at least qkv_act_image_bytes and
+    qkv_act_exp_image_bytes bytes)."""
+    import torch
+    T, H = x.shape
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise QkvmxError("mx_block_quantize_staged takes fp32 or bf16 rows")
+    dt = DTYPE_BF16 if x.dtype == torch.bfloat16 else DTYPE_F32
+    _check(lib().mx_block_quantize_staged(_ptr(x), dt, T, H, _ptr(act_image), _nbytes(act_image),
+                                          _ptr(exp_image), _nbytes(exp_image), _stream(stream)),
+           "mx_block_quantize_staged")
+
+
+def rmsnorm_mx_block_quantize_staged(hidden, gamma, eps: float, act_image, exp_image,
+                                     residual=None, residual_out=None, norm_out=None,
+                                     unpadded_h: int = 0, stream=None):
+    """bf16 hidden [T, H] (+ residual) -> residual_out, staged MX block-32 codes and exponents,
+    and (norm_out) the bf16 normed rows."""
+    T, H = hidden.shape
+    _check(lib().rmsnorm_mx_block_quantize_staged(_ptr(hidden), _ptr(residual), _ptr(gamma),
+                                                  float(eps), T, H, unpadded_h,
+                                                  _ptr(residual_out), _ptr(act_image),
+                                                  _nbytes(act_image), _ptr(exp_image),
+                                                  _nbytes(exp_image), _ptr(norm_out),
+                                                  _stream(stream)),
+           "rmsnorm_mx_block_quantize_staged")
+
+
+def qkv_mx_project_staged(act_image, exp_image, w_packed, out, *, T: int, H: int,
+                          num_heads: int, num_kv_heads: int, head_dim: int, channel_scale=None,
+                          bias=None, ssq=None, workspace=None, layout: int = LAYOUT_BSD,
+                          stream=None):
+    """Pass 1 on staged MX block-32 activations.  Output as qkv_mx_project."""
+    ws_ptr, ws_n = (None, 0) if workspace is None else (_ptr(workspace), _nbytes(workspace))
+    _check(lib().qkv_mx_project_staged(_ptr(act_image), _nbytes(act_image), _ptr(exp_image),
+                                       _nbytes(exp_image), _ptr(w_packed), _ptr(channel_scale),
+                                       _ptr(bias), T, H, num_heads, num_kv_heads, head_dim,
+                                       layout, _ptr(out), _ptr(ssq), ws_ptr, ws_n,
+                                       _stream(stream)), "qkv_mx_project_staged")
 
 
 def qkv_mx_workspace_bytes(T: int, H: int, I: int) -> int:

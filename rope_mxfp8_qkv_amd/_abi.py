@@ -54,6 +54,12 @@ SIGNATURES = {
     "qkv_staged_workspace_bytes": (c_sz, [c_i64, c_i64]),
     "qkv_rowmx_project_staged": (c_i32, [c_vp, c_sz, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i32,
                                          c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "qkv_act_exp_image_bytes": (c_sz, [c_i64, c_i64]),
+    "mx_block_quantize_staged": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_vp, c_sz, c_vp, c_sz, c_vp]),
+    "rmsnorm_mx_block_quantize_staged": (c_i32, [c_vp, c_vp, c_vp, c_f, c_i64, c_i64, c_i64, c_vp,
+                                                 c_vp, c_sz, c_vp, c_sz, c_vp, c_vp]),
+    "qkv_mx_project_staged": (c_i32, [c_vp, c_sz, c_vp, c_sz, c_vp, c_vp, c_vp, c_i64, c_i64, c_i32,
+                                      c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "qkvmx_mfma_rate_probe": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
     "qk_norm_rope_apply": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_i32, c_i32,
                                    c_f, c_u32, c_i32, c_vp]),

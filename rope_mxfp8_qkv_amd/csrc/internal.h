@@ -107,6 +107,17 @@ hipError_t launch_rmsnorm_quantize_staged(const uint16_t* hid, const uint16_t* r
                                           const uint16_t* gamma, float eps, int64_t T, int64_t H,
                                           int64_t Hu, uint16_t* res_out, uint8_t* img,
                                           float* row_scale, hipStream_t s);
+hipError_t launch_mx_quantize_staged(const void* x, int dtype, int64_t T, int64_t H,
+                                     uint8_t* img, uint32_t* eimg, hipStream_t s);
+hipError_t launch_rmsnorm_mx_staged(const uint16_t* hid, const uint16_t* res,
+                                    const uint16_t* gamma, float eps, int64_t T, int64_t H,
+                                    int64_t Hu, uint16_t* res_out, uint8_t* img, uint32_t* eimg,
+                                    uint16_t* norm_out, hipStream_t s);
+hipError_t launch_project_mx_staged(const uint8_t* img, const uint32_t* eimg,
+                                    const uint8_t* w_packed, const float* chan_scale,
+                                    const uint16_t* bias, int64_t T, int64_t H, int64_t I,
+                                    int64_t Iq, int64_t Ik, int64_t d, bool nbsd, uint16_t* out,
+                                    float* ssq, uint8_t* ws, hipStream_t s);
 hipError_t launch_project_staged(const uint8_t* img, const float* row_scale,
                                  const uint8_t* w_packed, const float* chan_scale,
                                  const uint16_t* bias, int64_t T, int64_t H, int64_t I, int64_t Iq,

@@ -33,7 +33,7 @@
 //    transposed through LDS so every global store is a coalesced 16-byte vector along a token
 //    row.  A small second kernel adds the partials in a fixed order (deterministic, no atomics).
 //  * Tile order and scheduling: one persistent block per CU.  The tiles are split into 8
-//    contiguous ranges, one per XCD, walked in groups of 8 token tiles x all channel tiles;
+//    contiguous ranges, one per XCD, walked in groups of 4 token tiles x all channel tiles;
 //    a block claims tiles one at a time from its own XCD's range (an atomic counter), so the
 //    tiles resident on one XCD at any time share activation rows and weight columns in its
 //    L2, and it prefetches the next tile's first stages while the current tile's epilogue
@@ -57,7 +57,7 @@ typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kGroupM = 8;                         // token tiles per raster group
+constexpr int kGroupM = 4;                         // token tiles per raster group
 constexpr int kXcds = 8;
 constexpr int kHwRegXccId = 20 | (31 << 11);        // s_getreg operand: XCC_ID, bits [31:0]
 constexpr int kBufs = 4;                           // LDS stage buffers

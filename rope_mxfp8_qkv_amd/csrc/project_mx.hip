@@ -1,5 +1,7 @@
-// Launcher of the projection on MX block-32 activations (qkv_mx_project): codes and exponents
-// re-laid per call, then the persistent projection kernel with per-block activation exponents.
+// Launchers of the projection on MX block-32 activations: from natural-order codes and
+// exponents (qkv_mx_project: both re-laid per call, then the persistent projection kernel with
+// per-block activation exponents) and from staged ones (qkv_mx_project_staged: written by a
+// staged producer in the kernel's layouts, so no re-layout).
 #include "project_kernel.h"
 
 namespace qkvmx {
@@ -24,6 +26,22 @@ hipError_t launch_project_mx(const uint8_t* a_codes, int64_t a_stride, const uin
   dim3 sg(2, (unsigned)(a.KS / 4), (unsigned)a.tiles_m);
   hipLaunchKernelGGL(act_scale_repack_kernel, sg, dim3(256), 0, s, a_e8, e_stride, T, H,
                      reinterpret_cast<uint32_t*>(ws + mx_scale_image_offset(T, H)));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_core<true>(a, chan_scale, bias, nbsd, ssq, s);
+}
+
+hipError_t launch_project_mx_staged(const uint8_t* img, const uint32_t* eimg,
+                                    const uint8_t* w_packed, const float* chan_scale,
+                                    const uint16_t* bias, int64_t T, int64_t H, int64_t I,
+                                    int64_t Iq, int64_t Ik, int64_t d, bool nbsd, uint16_t* out,
+                                    float* ssq, uint8_t* ws, hipStream_t s) {
+  ProjectArgs a = common_args(w_packed, chan_scale, bias, T, H, I, Iq, Ik, d, out);
+  a.x_img = img;
+  a.x_scales = reinterpret_cast<const uint8_t*>(eimg);
+  a.ws = ssq ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ctr = reinterpret_cast<unsigned*>(ws + staged_counters_offset(T, I));
+  hipLaunchKernelGGL(reset_counters_kernel, dim3(1), dim3(64), 0, s, a.ctr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_core<true>(a, chan_scale, bias, nbsd, ssq, s);

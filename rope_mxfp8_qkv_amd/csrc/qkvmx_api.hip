@@ -186,6 +186,54 @@ qkvmx_status rmsnorm_mx_block_quantize(const uint16_t* hidden, const uint16_t* r
                                       codes_out, e8m0_out, norm_out, stream), "rmsnorm_mx_block_quantize");
 }
 
+size_t qkv_act_exp_image_bytes(int64_t T, int64_t H) {
+  if (T <= 0 || H <= 0 || H % 32) return 0;
+  return mx_scale_image_bytes(T, H);
+}
+
+qkvmx_status mx_block_quantize_staged(const void* x, int32_t x_dtype, int64_t T, int64_t H,
+                                      uint8_t* act_image, size_t image_bytes, uint32_t* exp_image,
+                                      size_t exp_image_bytes, hipStream_t stream) {
+  const char* fn = "mx_block_quantize_staged";
+  if (!x || !act_image || !exp_image) return fail(QKVMX_ERR_NULL, "%s: null pointer", fn);
+  if (x_dtype != QKVMX_DTYPE_F32 && x_dtype != QKVMX_DTYPE_BF16) return fail(QKVMX_ERR_ARG, "%s: bad dtype", fn);
+  if (T <= 0 || H <= 0 || H % 32) return fail(QKVMX_ERR_SHAPE, "%s: need T > 0, H %% 32 == 0", fn);
+  if (H > kMaxRowH) return fail(QKVMX_ERR_UNSUPPORTED, "%s: H > %lld", fn, (long long)kMaxRowH);
+  if (ceil_div(T, 256) * 256 > INT32_MAX) return fail(QKVMX_ERR_UNSUPPORTED, "%s: T too large", fn);
+  if (image_bytes < act_image_bytes(T, H) || exp_image_bytes < mx_scale_image_bytes(T, H))
+    return fail(QKVMX_ERR_SHAPE, "%s: images need %zu and %zu bytes", fn, act_image_bytes(T, H), mx_scale_image_bytes(T, H));
+  if (!aligned(x, 16) || !aligned(act_image, 16) || !aligned(exp_image, 16))
+    return fail(QKVMX_ERR_ALIGN, "%s: x, act_image and exp_image 16-byte aligned", fn);
+  return hip_status(launch_mx_quantize_staged(x, x_dtype, T, H, act_image, exp_image, stream), fn);
+}
+
+qkvmx_status rmsnorm_mx_block_quantize_staged(const uint16_t* hidden, const uint16_t* residual,
+                                              const uint16_t* gamma, float eps, int64_t T,
+                                              int64_t H, int64_t unpadded_H,
+                                              uint16_t* residual_out, uint8_t* act_image,
+                                              size_t image_bytes, uint32_t* exp_image,
+                                              size_t exp_image_bytes, uint16_t* norm_out,
+                                              hipStream_t stream) {
+  const char* fn = "rmsnorm_mx_block_quantize_staged";
+  if (!hidden || !gamma || !act_image || !exp_image) return fail(QKVMX_ERR_NULL, "%s: null pointer", fn);
+  if (residual && !residual_out) return fail(QKVMX_ERR_ARG, "%s: residual_out is required with a residual", fn);
+  if (!residual && residual_out) return fail(QKVMX_ERR_ARG, "%s: residual_out given without a residual", fn);
+  if (T <= 0 || H <= 0 || H % 32) return fail(QKVMX_ERR_SHAPE, "%s: need T > 0, H %% 32 == 0", fn);
+  if (unpadded_H < 0 || unpadded_H > H) return fail(QKVMX_ERR_SHAPE, "%s: unpadded_H outside [0, H]", fn);
+  if (!(eps >= 0.0f)) return fail(QKVMX_ERR_ARG, "%s: eps must be >= 0", fn);
+  if (H > kMaxRowH) return fail(QKVMX_ERR_UNSUPPORTED, "%s: H > %lld", fn, (long long)kMaxRowH);
+  if (ceil_div(T, 256) * 256 > INT32_MAX) return fail(QKVMX_ERR_UNSUPPORTED, "%s: T too large", fn);
+  if (image_bytes < act_image_bytes(T, H) || exp_image_bytes < mx_scale_image_bytes(T, H))
+    return fail(QKVMX_ERR_SHAPE, "%s: images need %zu and %zu bytes", fn, act_image_bytes(T, H), mx_scale_image_bytes(T, H));
+  if (!aligned(hidden, 16) || !aligned(gamma, 16) || (residual && !aligned(residual, 16)) ||
+      (residual_out && !aligned(residual_out, 16)) || (norm_out && !aligned(norm_out, 16)) ||
+      !aligned(act_image, 16) || !aligned(exp_image, 16))
+    return fail(QKVMX_ERR_ALIGN, "%s: bf16 tensors, act_image and exp_image 16-byte aligned", fn);
+  const int64_t Hu = unpadded_H ? unpadded_H : H;
+  return hip_status(launch_rmsnorm_mx_staged(hidden, residual, gamma, eps, T, H, Hu, residual_out,
+                                             act_image, exp_image, norm_out, stream), fn);
+}
+
 size_t qkvmx_workspace_bytes(int64_t T, int64_t H, int64_t I) {
   if (T <= 0 || H <= 0 || I <= 0 || H % 32) return 0;
   return workspace_total_bytes(T, H, I);
@@ -358,6 +406,40 @@ qkvmx_status qkv_mx_project(const uint8_t* a_codes, int64_t a_row_stride, const 
                                       (const uint8_t*)w_packed, w_channel_scale, bias, T, H, I,
                                       Iq, Ik, head_dim, layout == QKVMX_LAYOUT_NBSD, out, ssq,
                                       (uint8_t*)workspace, stream), "qkv_mx_project");
+}
+
+qkvmx_status qkv_mx_project_staged(const uint8_t* act_image, size_t image_bytes,
+                                   const uint32_t* exp_image, size_t exp_image_bytes,
+                                   const void* w_packed, const float* w_channel_scale,
+                                   const uint16_t* bias, int64_t T, int64_t H, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t layout,
+                                   uint16_t* out, float* ssq, void* workspace, size_t ws_bytes,
+                                   hipStream_t stream) {
+  const char* fn = "qkv_mx_project_staged";
+  if (!act_image || !exp_image || !w_packed || !out) return fail(QKVMX_ERR_NULL, "%s: null pointer", fn);
+  if (!workspace) return fail(QKVMX_ERR_WORKSPACE, "%s: workspace is required", fn);
+  if (T <= 0 || H <= 0 || H % 32) return fail(QKVMX_ERR_SHAPE, "%s: need T > 0, H %% 32 == 0", fn);
+  if (num_heads < 1 || num_kv_heads < 0 || head_dim <= 0 || head_dim % 16)
+    return fail(QKVMX_ERR_SHAPE, "%s: need num_heads >= 1, num_kv_heads >= 0, head_dim %% 16 == 0", fn);
+  if (layout != QKVMX_LAYOUT_BSD && layout != QKVMX_LAYOUT_NBSD)
+    return fail(QKVMX_ERR_ARG, "%s: layout must be QKVMX_LAYOUT_BSD or QKVMX_LAYOUT_NBSD", fn);
+  if (image_bytes < act_image_bytes(T, H) || exp_image_bytes < mx_scale_image_bytes(T, H))
+    return fail(QKVMX_ERR_SHAPE, "%s: images need %zu and %zu bytes", fn, act_image_bytes(T, H), mx_scale_image_bytes(T, H));
+  const int64_t I = (int64_t)(num_heads + 2 * (int64_t)num_kv_heads) * head_dim;
+  if (I * 2 * 256 >= kMaxOffset) return fail(QKVMX_ERR_UNSUPPORTED, "%s: I must be < 2^22", fn);
+  if (layout == QKVMX_LAYOUT_NBSD && 2 * ((256 + (int64_t)head_dim) * T + 257 * (int64_t)head_dim) >= kMaxOffset)
+    return fail(QKVMX_ERR_UNSUPPORTED, "%s: NBSd needs 2 ((256 + head_dim) T + 257 head_dim) < 2^31", fn);
+  if (ws_bytes < staged_workspace_total_bytes(T, I))
+    return fail(QKVMX_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, staged_workspace_total_bytes(T, I));
+  if (!aligned(act_image, 256) || !aligned(exp_image, 256) || !aligned(w_packed, 256) ||
+      (w_channel_scale && !aligned(w_channel_scale, 16)) || (bias && !aligned(bias, 8)) ||
+      !aligned(out, 16) || (ssq && !aligned(ssq, 8)) || !aligned(workspace, 256))
+    return fail(QKVMX_ERR_ALIGN, "%s: alignment (images 256, w_packed 256, channel scale 16, bias 8, out 16, ssq 8, workspace 256)", fn);
+  const int64_t Iq = (int64_t)num_heads * head_dim, Ik = (int64_t)num_kv_heads * head_dim;
+  return hip_status(launch_project_mx_staged(act_image, exp_image, (const uint8_t*)w_packed,
+                                             w_channel_scale, bias, T, H, I, Iq, Ik, head_dim,
+                                             layout == QKVMX_LAYOUT_NBSD, out, ssq,
+                                             (uint8_t*)workspace, stream), fn);
 }
 
 qkvmx_status qk_norm_rope_apply(uint16_t* qkv, const float* ssq, const uint16_t* q_gamma,

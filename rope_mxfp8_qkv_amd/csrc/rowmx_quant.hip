@@ -269,10 +269,12 @@ __global__ void __launch_bounds__(1024) rmsnorm_quantize_kernel(
 // E = max(biased exponent of amax - 8, 0) (floor(log2 amax) - 8 + 127, clamped at 0; amax < 2^-119
 // or zero gives 0), codes = E4M3 RNE saturating of y * 2^(127 - E) (a power-of-two scaling,
 // exact for every value that does not round to zero); an all-zero block stores zero codes.
-// Codes go to codes_row (8 bytes per chunk), exponents through LDS to e8_row (dword stores).
-__device__ __forceinline__ void mx_encode_store(const float (&y)[kCpt][kChunk], int64_t H,
-                                                uint8_t* __restrict__ codes_row,
-                                                uint8_t* __restrict__ e8_row, uint8_t* sh_e) {
+// Codes go to chunk_at(c) (8 bytes per chunk; chunks in [H / 8, pad_chunks) get zero codes),
+// exponents to sh_e[block] in LDS; the caller stores them after the barrier that ends this.
+template <typename ChunkAt>
+__device__ __forceinline__ void mx_encode_codes(const float (&y)[kCpt][kChunk], int64_t H,
+                                                ChunkAt chunk_at, int64_t pad_chunks,
+                                                uint8_t* sh_e) {
   const int64_t nchunks = H / kChunk;
 #pragma unroll
   for (int k = 0; k < kCpt; ++k) {
@@ -294,11 +296,18 @@ __device__ __forceinline__ void mx_encode_store(const float (&y)[kCpt][kChunk], 
 #pragma unroll
         for (int e = 0; e < 4; ++e) hi |= f32_to_e4m3(y[k][4 + e] * inv) << (8 * e);
       }
-      __builtin_nontemporal_store(u32x2_t{lo, hi}, reinterpret_cast<u32x2_t*>(codes_row + c * kChunk));
+      __builtin_nontemporal_store(u32x2_t{lo, hi}, reinterpret_cast<u32x2_t*>(chunk_at(c)));
       if ((c & 3) == 0) sh_e[c >> 2] = (uint8_t)E;
+    } else if (c < pad_chunks) {
+      __builtin_nontemporal_store(u32x2_t{0u, 0u}, reinterpret_cast<u32x2_t*>(chunk_at(c)));
     }
   }
   __syncthreads();
+}
+
+// The exponents of one row, natural order: e8_row[b] = exponent of elements [32 b, 32 b + 32).
+__device__ __forceinline__ void mx_store_exponents(int64_t H, uint8_t* __restrict__ e8_row,
+                                                   const uint8_t* sh_e) {
   if (H % 128 == 0) {                              // whole dwords (the row start is 4-aligned)
     for (int64_t i = threadIdx.x; i < H / 128; i += blockDim.x)
       reinterpret_cast<uint32_t*>(e8_row)[i] = reinterpret_cast<const uint32_t*>(sh_e)[i];
@@ -307,13 +316,41 @@ __device__ __forceinline__ void mx_encode_store(const float (&y)[kCpt][kChunk], 
   }
 }
 
-// y = x (fp32 or bf16 rows), MX block-32 encoded.
-template <bool BF16>
-__global__ void __launch_bounds__(1024) mx_quantize_kernel(const void* __restrict__ x, int64_t H,
-                                                            uint8_t* __restrict__ codes,
-                                                            uint8_t* __restrict__ e8) {
+// The exponents of row m in the staged exponent image [MT][S][256][2] dwords (S = KS / 4
+// supersteps of 256 elements): byte q of dword g of superstep s = exponent of block
+// 8 s + 2 q + g, 127 (2^0) for blocks past H / 32; sh_e null: a row past T (all 127).
+__device__ __forceinline__ void mx_store_exponents_staged(int64_t H, uint32_t* __restrict__ eimg,
+                                                          int64_t m, int S, const uint8_t* sh_e) {
+  const int64_t nblocks = H / 32;
+  uint32_t* row = eimg + ((m / kTileM) * S * kTileM + (m & (kTileM - 1))) * 2;
+  for (int i = threadIdx.x; i < 2 * S; i += blockDim.x) {
+    const int sidx = i >> 1, g = i & 1;
+    uint32_t w = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t b = 8 * (int64_t)sidx + 2 * q + g;
+      const uint32_t e = (sh_e && b < nblocks) ? sh_e[b] : 127u;
+      w |= e << (8 * q);
+    }
+    row[(int64_t)sidx * kTileM * 2 + g] = w;
+  }
+}
+
+// y = x (fp32 or bf16 rows), MX block-32 encoded: codes [T, H] and exponents [T, H / 32], or
+// with STAGED the codes in the stage-image layout and the exponents in the staged exponent
+// image (grid: T rows rounded up to whole 256-row tiles; rows past T get zero codes and
+// exponents 127).
+template <bool BF16, bool STAGED>
+__global__ void __launch_bounds__(1024) mx_quantize_kernel(const void* __restrict__ x, int64_t T,
+                                                            int64_t H, uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ e8, int KS) {
   __shared__ __attribute__((aligned(4))) uint8_t sh_e[kMaxWaves * 64 * kCpt * kChunk / 32];
   const int64_t row = blockIdx.x;
+  if (STAGED && row >= T) {
+    staged_zero_row(codes, row, KS);
+    mx_store_exponents_staged(H, reinterpret_cast<uint32_t*>(e8), row, KS / 4, nullptr);
+    return;
+  }
   const int64_t nchunks = H / kChunk;
   float y[kCpt][kChunk];
 #pragma unroll
@@ -334,20 +371,34 @@ __global__ void __launch_bounds__(1024) mx_quantize_kernel(const void* __restric
       }
     }
   }
-  mx_encode_store(y, H, codes + row * H, e8 + row * (H / 32), sh_e);
+  if (STAGED) {
+    const StagedRow d = staged_row(codes, nullptr, row, KS);
+    mx_encode_codes(y, H, [&](int64_t c) { return d.chunk(c); }, d.padded, sh_e);
+    mx_store_exponents_staged(H, reinterpret_cast<uint32_t*>(e8), row, KS / 4, sh_e);
+  } else {
+    uint8_t* crow = codes + row * H;
+    mx_encode_codes(y, H, [&](int64_t c) { return crow + c * kChunk; }, 0, sh_e);
+    mx_store_exponents(H, e8 + row * (H / 32), sh_e);
+  }
 }
 
 // Residual add + RMSNorm (the steps of rmsnorm_quantize_kernel), then MX block-32 encoding of
-// y and, with EMIT, y rounded to bf16 (RNE) into norm_out.
-template <bool RES, bool EMIT>
+// y (natural or, with STAGED, staged layouts as mx_quantize_kernel) and, with EMIT, y rounded
+// to bf16 (RNE) into norm_out.
+template <bool RES, bool EMIT, bool STAGED>
 __global__ void __launch_bounds__(1024) rmsnorm_mx_kernel(
     const uint16_t* __restrict__ hid, const uint16_t* __restrict__ res,
-    const uint16_t* __restrict__ gamma, float eps, int64_t H, int64_t Hu,
+    const uint16_t* __restrict__ gamma, float eps, int64_t T, int64_t H, int64_t Hu,
     uint16_t* __restrict__ res_out, uint8_t* __restrict__ codes, uint8_t* __restrict__ e8,
-    uint16_t* __restrict__ norm_out) {
+    uint16_t* __restrict__ norm_out, int KS) {
   __shared__ double shd[kMaxWaves];
   __shared__ __attribute__((aligned(4))) uint8_t sh_e[kMaxWaves * 64 * kCpt * kChunk / 32];
   const int64_t row = blockIdx.x;
+  if (STAGED && row >= T) {
+    staged_zero_row(codes, row, KS);
+    mx_store_exponents_staged(H, reinterpret_cast<uint32_t*>(e8), row, KS / 4, nullptr);
+    return;
+  }
   float y[kCpt][kChunk];
   normed_row<RES>(hid, res, gamma, eps, H, Hu, res_out, row, y, shd);
   if (EMIT) {
@@ -361,7 +412,15 @@ __global__ void __launch_bounds__(1024) rmsnorm_mx_kernel(
                        pack_bf16x2(y[k][4], y[k][5]), pack_bf16x2(y[k][6], y[k][7]));
     }
   }
-  mx_encode_store(y, H, codes + row * H, e8 + row * (H / 32), sh_e);
+  if (STAGED) {
+    const StagedRow d = staged_row(codes, nullptr, row, KS);
+    mx_encode_codes(y, H, [&](int64_t c) { return d.chunk(c); }, d.padded, sh_e);
+    mx_store_exponents_staged(H, reinterpret_cast<uint32_t*>(e8), row, KS / 4, sh_e);
+  } else {
+    uint8_t* crow = codes + row * H;
+    mx_encode_codes(y, H, [&](int64_t c) { return crow + c * kChunk; }, 0, sh_e);
+    mx_store_exponents(H, e8 + row * (H / 32), sh_e);
+  }
 }
 
 unsigned block_threads(int64_t H) {
@@ -427,24 +486,57 @@ hipError_t launch_mx_quantize(const void* x, int dtype, int64_t T, int64_t H, ui
                               uint8_t* e8, hipStream_t s) {
   const dim3 grid((unsigned)T), block(block_threads(H));
   if (dtype == 1)
-    hipLaunchKernelGGL(mx_quantize_kernel<true>, grid, block, 0, s, x, H, codes, e8);
+    hipLaunchKernelGGL((mx_quantize_kernel<true, false>), grid, block, 0, s, x, T, H, codes, e8, 0);
   else
-    hipLaunchKernelGGL(mx_quantize_kernel<false>, grid, block, 0, s, x, H, codes, e8);
+    hipLaunchKernelGGL((mx_quantize_kernel<false, false>), grid, block, 0, s, x, T, H, codes, e8, 0);
   return hipGetLastError();
 }
+
+hipError_t launch_mx_quantize_staged(const void* x, int dtype, int64_t T, int64_t H,
+                                     uint8_t* img, uint32_t* eimg, hipStream_t s) {
+  const dim3 grid((unsigned)(ceil_div(T, kTileM) * kTileM)), block(block_threads(H));
+  const int KS = (int)packed_stages(H);
+  uint8_t* e = reinterpret_cast<uint8_t*>(eimg);
+  if (dtype == 1)
+    hipLaunchKernelGGL((mx_quantize_kernel<true, true>), grid, block, 0, s, x, T, H, img, e, KS);
+  else
+    hipLaunchKernelGGL((mx_quantize_kernel<false, true>), grid, block, 0, s, x, T, H, img, e, KS);
+  return hipGetLastError();
+}
+
+namespace {
+
+template <bool STAGED>
+hipError_t launch_rmsnorm_mx_any(const uint16_t* hid, const uint16_t* res, const uint16_t* gamma,
+                                 float eps, int64_t T, int64_t H, int64_t Hu, uint16_t* res_out,
+                                 uint8_t* codes, uint8_t* e8, uint16_t* norm_out, hipStream_t s) {
+  const dim3 grid((unsigned)(STAGED ? ceil_div(T, kTileM) * kTileM : T)), block(block_threads(H));
+  const int KS = STAGED ? (int)packed_stages(H) : 0;
+  const int v = (res ? 2 : 0) | (norm_out ? 1 : 0);
+  switch (v) {
+    case 0: hipLaunchKernelGGL((rmsnorm_mx_kernel<false, false, STAGED>), grid, block, 0, s, hid, res, gamma, eps, T, H, Hu, res_out, codes, e8, norm_out, KS); break;
+    case 1: hipLaunchKernelGGL((rmsnorm_mx_kernel<false, true, STAGED>), grid, block, 0, s, hid, res, gamma, eps, T, H, Hu, res_out, codes, e8, norm_out, KS); break;
+    case 2: hipLaunchKernelGGL((rmsnorm_mx_kernel<true, false, STAGED>), grid, block, 0, s, hid, res, gamma, eps, T, H, Hu, res_out, codes, e8, norm_out, KS); break;
+    default: hipLaunchKernelGGL((rmsnorm_mx_kernel<true, true, STAGED>), grid, block, 0, s, hid, res, gamma, eps, T, H, Hu, res_out, codes, e8, norm_out, KS); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
 
 hipError_t launch_rmsnorm_mx(const uint16_t* hid, const uint16_t* res, const uint16_t* gamma,
                              float eps, int64_t T, int64_t H, int64_t Hu, uint16_t* res_out,
                              uint8_t* codes, uint8_t* e8, uint16_t* norm_out, hipStream_t s) {
-  const dim3 grid((unsigned)T), block(block_threads(H));
-  const int v = (res ? 2 : 0) | (norm_out ? 1 : 0);
-  switch (v) {
-    case 0: hipLaunchKernelGGL((rmsnorm_mx_kernel<false, false>), grid, block, 0, s, hid, res, gamma, eps, H, Hu, res_out, codes, e8, norm_out); break;
-    case 1: hipLaunchKernelGGL((rmsnorm_mx_kernel<false, true>), grid, block, 0, s, hid, res, gamma, eps, H, Hu, res_out, codes, e8, norm_out); break;
-    case 2: hipLaunchKernelGGL((rmsnorm_mx_kernel<true, false>), grid, block, 0, s, hid, res, gamma, eps, H, Hu, res_out, codes, e8, norm_out); break;
-    default: hipLaunchKernelGGL((rmsnorm_mx_kernel<true, true>), grid, block, 0, s, hid, res, gamma, eps, H, Hu, res_out, codes, e8, norm_out); break;
-  }
-  return hipGetLastError();
+  return launch_rmsnorm_mx_any<false>(hid, res, gamma, eps, T, H, Hu, res_out, codes, e8,
+                                      norm_out, s);
+}
+
+hipError_t launch_rmsnorm_mx_staged(const uint16_t* hid, const uint16_t* res,
+                                    const uint16_t* gamma, float eps, int64_t T, int64_t H,
+                                    int64_t Hu, uint16_t* res_out, uint8_t* img, uint32_t* eimg,
+                                    uint16_t* norm_out, hipStream_t s) {
+  return launch_rmsnorm_mx_any<true>(hid, res, gamma, eps, T, H, Hu, res_out, img,
+                                     reinterpret_cast<uint8_t*>(eimg), norm_out, s);
 }
 
 }  // namespace qkvmx

@@ -160,3 +160,21 @@ def unstage(image, rows: np.ndarray, H: int) -> np.ndarray:
     import torch
     idx = torch.as_tensor(staged_index(rows, H).reshape(-1), device=image.device)
     return image[idx].reshape(len(rows), H).cpu().numpy()
+
+
+def staged_exp_index(rows: np.ndarray, H: int):
+    """(dword, byte) positions, in the staged MX exponent image, of the exponents of `rows`
+    (blocks 0..H/32-1): row t, block b = 8 s + 2 q + g at dword
+    ((t / 256 * S + s) * 256 + t % 256) * 2 + g, byte q; S = ceil(H / 256) (include/qkvmx.h)."""
+    S = -(-H // 256)
+    t = np.asarray(rows, dtype=np.int64)[:, None]
+    b = np.arange(H // 32, dtype=np.int64)[None, :]
+    s, q, g = b // 8, (b % 8) // 2, b % 2
+    return (((t // 256) * S + s) * 256 + t % 256) * 2 + g, q
+
+
+def unstage_exp(exp_image, rows: np.ndarray, H: int) -> np.ndarray:
+    """Exponents [len(rows), H / 32] from a staged exponent image (int32 device tensor)."""
+    dw, q = staged_exp_index(rows, H)
+    words = exp_image.view(-1).cpu().numpy().view(np.uint32)[dw]
+    return ((words >> (8 * q).astype(np.uint32)) & 0xFF).astype(np.uint8)

@@ -181,6 +181,35 @@ def test_staged_path_validation():
     assert L.rmsnorm_mx_quantize_staged(None, None, P, 1e-6, 4, 256, 0, None, P, 1 << 20, P, None) == 1
 
 
+def test_mx_staged_validation():
+    L = _lib()
+    # exponent image: 296 token tiles x 20 supersteps x 256 rows x 2 dwords
+    assert L.qkv_act_exp_image_bytes(75600, 5120) == 296 * 20 * 256 * 8
+    assert L.qkv_act_exp_image_bytes(300, 2080) == 2 * 9 * 256 * 8
+    assert L.qkv_act_exp_image_bytes(4, 100) == 0
+    big = 1 << 30
+    # (x, dtype, T, H, image, image_bytes, exp_image, exp_bytes, stream)
+    assert L.mx_block_quantize_staged(P, 0, 4, 256, P, big, None, big, None) == 1
+    assert L.mx_block_quantize_staged(P, 2, 4, 256, P, big, P, big, None) == 4
+    assert L.mx_block_quantize_staged(P, 0, 4, 100, P, big, P, big, None) == 2
+    assert L.mx_block_quantize_staged(P, 0, 4, 256, P, big, P, 100, None) == 2
+    assert L.mx_block_quantize_staged(P, 0, 4, 256, P, big, P + 4, big, None) == 3
+    # (hidden, residual, gamma, eps, T, H, Hu, residual_out, image, ib, exp, eb, norm_out, s)
+    assert L.rmsnorm_mx_block_quantize_staged(P, P, P, 1e-6, 4, 256, 0, None, P, big, P, big, None, None) == 4
+    assert L.rmsnorm_mx_block_quantize_staged(P, None, P, 1e-6, 4, 256, 0, None, P, 10, P, big, None, None) == 2
+    assert L.rmsnorm_mx_block_quantize_staged(P, None, P, 1e-6, 4, 256, 0, None, P, big, P, big, P + 8, None) == 3
+    a = dict(act_image=P, image_bytes=big, exp_image=P, exp_bytes=big, w_packed=P,
+             w_channel_scale=None, bias=None, T=4, H=256, num_heads=2, num_kv_heads=2,
+             head_dim=64, layout=0, out=P, ssq=None, workspace=P, ws_bytes=big, stream=None)
+    call = lambda **kw: L.qkv_mx_project_staged(*{**a, **kw}.values())
+    assert call(exp_image=None) == 1
+    assert call(exp_bytes=8) == 2
+    assert call(layout=5) == 4
+    assert call(workspace=None) == 5
+    assert call(ws_bytes=8) == 5
+    assert call(exp_image=P + 16) == 3
+
+
 def test_calibration_probe_validation():
     L = _lib()
     assert L.qkvmx_mfma_rate_probe(0, 10, 1, P, P, None) == 2

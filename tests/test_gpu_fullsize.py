@@ -183,10 +183,12 @@ def test_fullsize_staged_producer_then_self_attention():
     _run_self_attention(synth.CONFIGS[5].calls[0], producer=True, staged=True)
 
 
-def test_fullsize_mx_producer_then_self_attention():
+@pytest.mark.parametrize("staged", [False, True], ids=["natural", "staged"])
+def test_fullsize_mx_producer_then_self_attention(staged):
     """MX block-32 path at the full video shape: bf16 hidden + residual -> residual add +
     RMSNorm + E4M3 codes with per-32 exponents (and the bf16 normed rows) -> projection with
-    per-block activation exponents -> norm + 3-axis RoPE."""
+    per-block activation exponents -> norm + 3-axis RoPE; natural-order codes and exponents, or
+    staged in the projection's layouts (the benchmark's --act mx step)."""
     import torch
     q = __import__("rope_mxfp8_qkv_amd")
     q.lib()
@@ -196,20 +198,31 @@ def test_fullsize_mx_producer_then_self_attention():
     rows = sample_rows(p.T)
     print(f"[fullsize] {p.name} (MX block-32): T={p.T} H={p.H} I={p.I} rows={len(rows)}", flush=True)
     hid, res, gam = synth.producer_inputs(p.seed_id, p.T, p.H)
-    codes = torch.empty((p.T, p.H), dtype=torch.uint8, device=dev)
-    e8 = torch.empty((p.T, p.H // 32), dtype=torch.uint8, device=dev)
     res_out = torch.empty((p.T, p.H), dtype=torch.bfloat16, device=dev)
     norm = torch.empty((p.T, p.H), dtype=torch.bfloat16, device=dev)
-    q.rmsnorm_mx_block_quantize(G.bf16_dev(hid, dev), G.bf16_dev(gam, dev), 1e-6, codes, e8,
-                                residual=G.bf16_dev(res, dev), residual_out=res_out,
-                                norm_out=norm)
+    if staged:
+        img = torch.empty(q.qkv_act_image_bytes(p.T, p.H), dtype=torch.uint8, device=dev)
+        eimg = torch.empty(q.qkv_act_exp_image_bytes(p.T, p.H) // 4, dtype=torch.int32, device=dev)
+        q.rmsnorm_mx_block_quantize_staged(G.bf16_dev(hid, dev), G.bf16_dev(gam, dev), 1e-6, img,
+                                           eimg, residual=G.bf16_dev(res, dev),
+                                           residual_out=res_out, norm_out=norm)
+    else:
+        codes = torch.empty((p.T, p.H), dtype=torch.uint8, device=dev)
+        e8 = torch.empty((p.T, p.H // 32), dtype=torch.uint8, device=dev)
+        q.rmsnorm_mx_block_quantize(G.bf16_dev(hid, dev), G.bf16_dev(gam, dev), 1e-6, codes, e8,
+                                    residual=G.bf16_dev(res, dev), residual_out=res_out,
+                                    norm_out=norm)
     r_ref, c_ref, e_ref, n_ref, _ = oracle.rmsnorm_mx(hid[rows], res[rows], gam, 1e-6)
     del hid, res
     ti = _idx(rows, dev)
     G.check_equal(G.bf16_host(res_out[ti]), r_ref, "residual_out rows")
     G.check_equal(G.bf16_host(norm[ti]), n_ref, "bf16 norm rows")
-    G.check_equal(codes[ti].cpu().numpy(), c_ref, "MX code rows")
-    G.check_equal(e8[ti].cpu().numpy(), e_ref, "MX exponent rows")
+    if staged:
+        G.check_equal(G.unstage(img, rows, p.H), c_ref, "MX code rows")
+        G.check_equal(G.unstage_exp(eimg, rows, p.H), e_ref, "MX exponent rows")
+    else:
+        G.check_equal(codes[ti].cpu().numpy(), c_ref, "MX code rows")
+        G.check_equal(e8[ti].cpu().numpy(), e_ref, "MX exponent rows")
     del res_out, norm
     w = synth.weight(p)
     wcodes, we8, wp = gpu.weight(w)
@@ -219,10 +232,16 @@ def test_fullsize_mx_producer_then_self_attention():
     cos, sin = synth.rope_tables(p)
     out = torch.empty((p.T, p.I), dtype=torch.bfloat16, device=dev)
     ssq = torch.empty((p.T, 2), dtype=torch.float32, device=dev)
-    ws = torch.empty(q.qkv_mx_workspace_bytes(p.T, p.H, p.I), dtype=torch.uint8, device=dev)
-    q.qkv_mx_project(codes, e8, wp, out, H=p.H, num_heads=p.num_heads,
-                     num_kv_heads=p.num_kv_heads, head_dim=p.head_dim,
-                     bias=G.bf16_dev(bias, dev), ssq=ssq, workspace=ws)
+    if staged:
+        ws = torch.empty(q.qkv_staged_workspace_bytes(p.T, p.I), dtype=torch.uint8, device=dev)
+        q.qkv_mx_project_staged(img, eimg, wp, out, T=p.T, H=p.H, num_heads=p.num_heads,
+                                num_kv_heads=p.num_kv_heads, head_dim=p.head_dim,
+                                bias=G.bf16_dev(bias, dev), ssq=ssq, workspace=ws)
+    else:
+        ws = torch.empty(q.qkv_mx_workspace_bytes(p.T, p.H, p.I), dtype=torch.uint8, device=dev)
+        q.qkv_mx_project(codes, e8, wp, out, H=p.H, num_heads=p.num_heads,
+                         num_kv_heads=p.num_kv_heads, head_dim=p.head_dim,
+                         bias=G.bf16_dev(bias, dev), ssq=ssq, workspace=ws)
     seg = (p.num_heads + p.num_kv_heads) * p.head_dim
     v_before = out[ti, seg:].clone()
     fl = gpu.pass2(p, out, ssq, gq, gk, cos, sin)

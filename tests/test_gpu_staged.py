@@ -1,6 +1,6 @@
-"""GPU parity of the staged ROW_MX path: producers that write the codes in the projection's
-stage-image layout (plus fp32 row scales) and the projection that consumes them without a
-per-call re-layout.
+"""GPU parity of the staged paths: producers that write the codes in the projection's
+stage-image layout (plus fp32 row scales for ROW_MX, or an exponent image for MX block-32) and
+the projections that consume them without a per-call re-layout.
 
 Codes and scales are compared bit for bit with the oracle's ROW_MX rows (the image is read back
 through the layout formula of include/qkvmx.h, restated in gpu_common.staged_index); the padding
@@ -169,3 +169,142 @@ def test_projection_staged_repeated_calls_share_workspace():
         X, _ = oracle.project(codes[:T], sA[:T], inp.w_codes, inp.w_e8m0, None, inp.bias,
                               num_heads=2, num_kv_heads=2, head_dim=128)
         G.check_close(G.bf16_host(out), X, f"T={T} X")
+
+
+# ----------------------------------------------------------------------------------------------
+# MX block-32
+# ----------------------------------------------------------------------------------------------
+
+def _exp_image(q, T, H, dev):
+    import torch
+    n = q.qkv_act_exp_image_bytes(T, H)
+    return torch.full((n // 4,), 0x5A5A5A5A, dtype=torch.int32, device=dev)
+
+
+def _check_exp_padding(eimg, T, H):
+    """Every exponent byte outside the T x H/32 exponents is 127."""
+    host = eimg.cpu().numpy().view(np.uint8).reshape(-1)
+    used = np.zeros(host.size, dtype=bool)
+    dw, qb = G.staged_exp_index(np.arange(T), H)
+    used[(dw * 4 + qb).reshape(-1)] = True
+    bad = host[~used] != 127
+    assert not bad.any(), f"{int(bad.sum())} padding exponents are not 127"
+
+
+def _blocky(T, H, seed, spread=6):
+    """N(0,1) rows with a random power of two in 2^-spread .. 2^spread per 32-element block, a
+    zero block and a tiny block.  The projection tests use spread 2: one FP8 MFMA sums its 64
+    products to about 2^-12 of their absolute sum, so wide spreads produce outputs that cancel
+    below the bf16 tolerance on any encoding (the encoder tests use the wide spread)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x *= np.ldexp(1.0, rng.integers(-spread, spread + 1, (T, H // 32))).repeat(32, axis=1).astype(np.float32)
+    x[0, 32:64] = 0.0
+    if T > 1:
+        x[1, :32] *= np.float32(1e-30)
+    return x
+
+
+@pytest.mark.parametrize("dtype,H", [("f32", 2080), ("bf16", 5120)])
+def test_mx_block_quantize_staged_bit_exact(dtype, H):
+    import torch
+    q = _lib()
+    dev = G.torch_dev()
+    T = 300
+    x = _blocky(T, H, 13)
+    if dtype == "bf16":
+        bits = synth.to_bf16_bits(x)
+        x = synth.bf16_bits_to_f32(bits)
+        xd = G.bf16_dev(bits, dev)
+    else:
+        xd = G.to_dev(x, dev)
+    codes_ref, e8_ref = oracle.mx_block_quantize(x)
+    img, eimg = _image(q, T, H, dev), _exp_image(q, T, H, dev)
+    q.mx_block_quantize_staged(xd, img, eimg)
+    torch.cuda.synchronize()
+    G.check_equal(G.unstage(img, np.arange(T), H), codes_ref, "staged codes")
+    G.check_equal(G.unstage_exp(eimg, np.arange(T), H), e8_ref, "staged exponents")
+    _check_padding(img, T, H)
+    _check_exp_padding(eimg, T, H)
+
+
+@pytest.mark.parametrize("with_res,emit,Hu", [(True, True, 0), (False, False, 0), (True, True, 4000)])
+def test_rmsnorm_mx_block_staged_bit_exact(with_res, emit, Hu):
+    import torch
+    q = _lib()
+    dev = G.torch_dev()
+    T, H = 300, 5120
+    hid, res, gam = synth.producer_inputs(79, T, H)
+    if Hu:
+        hid[:, Hu:] = 0
+        res[:, Hu:] = 0
+    res_ref, codes_ref, e8_ref, norm_ref, _ = oracle.rmsnorm_mx(hid, res if with_res else None,
+                                                                gam, 1e-6, Hu)
+    img, eimg = _image(q, T, H, dev), _exp_image(q, T, H, dev)
+    res_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if with_res else None
+    norm = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if emit else None
+    q.rmsnorm_mx_block_quantize_staged(G.bf16_dev(hid, dev), G.bf16_dev(gam, dev), 1e-6, img,
+                                       eimg, residual=G.bf16_dev(res, dev) if with_res else None,
+                                       residual_out=res_out, norm_out=norm, unpadded_h=Hu)
+    torch.cuda.synchronize()
+    if with_res:
+        G.check_equal(G.bf16_host(res_out), res_ref, "residual_out")
+    if emit:
+        G.check_equal(G.bf16_host(norm), norm_ref, "bf16 norm output")
+    G.check_equal(G.unstage(img, np.arange(T), H), codes_ref, "staged codes")
+    G.check_equal(G.unstage_exp(eimg, np.arange(T), H), e8_ref, "staged exponents")
+    _check_padding(img, T, H)
+    _check_exp_padding(eimg, T, H)
+
+
+MX_STAGED_CASES = [
+    ("C1", synth.CONFIGS[1].calls[0], 0, False),
+    ("ragged-T-N-chan", G.custom_projection("mrn", T=300, H=512, nq=3, nkv=1, d=128), 0, True),
+    ("nbsd-ragged-H", G.custom_projection("mnb", T=200, H=352, nq=3, nkv=1, d=64), 1, False),
+    ("T1", G.custom_projection("mt1", T=1, H=256, nq=2, nkv=2, d=64), 0, False),
+]
+
+
+@pytest.mark.parametrize("name,p,layout,chan", MX_STAGED_CASES, ids=[c[0] for c in MX_STAGED_CASES])
+def test_mx_projection_staged_parity(name, p, layout, chan):
+    """Staged MX producer -> staged MX projection == natural-order MX producer -> MX projection
+    (bytes), and within tolerance of the oracle."""
+    import torch
+    q = _lib()
+    dev = G.torch_dev()
+    x = _blocky(p.T, p.H, 23, spread=2)
+    codes_ref, e8_ref = oracle.mx_block_quantize(x)
+    w_codes, w_e8m0 = oracle.mx_weight_quantize(synth.weight(p))
+    bias = synth.bias_bf16(p)
+    rng = np.random.default_rng(6)
+    cs = (0.5 + rng.random(p.I)).astype(np.float32) if chan else None
+    X, ssq_ref = oracle.project(codes_ref, None, w_codes, w_e8m0, cs, bias,
+                                num_heads=p.num_heads, num_kv_heads=p.num_kv_heads,
+                                head_dim=p.head_dim, a_e8m0=e8_ref)
+    wp = q.prepare_weight(G.to_dev(w_codes, dev), G.to_dev(w_e8m0, dev), p.H, p.I)
+    shape = (p.I // p.head_dim, p.T, p.head_dim) if layout else (p.T, p.I)
+    kw = dict(H=p.H, num_heads=p.num_heads, num_kv_heads=p.num_kv_heads, head_dim=p.head_dim,
+              channel_scale=None if cs is None else G.to_dev(cs, dev),
+              bias=G.bf16_dev(bias, dev), layout=layout)
+    xd = G.to_dev(x, dev)
+    codes = torch.empty((p.T, p.H), dtype=torch.uint8, device=dev)
+    e8 = torch.empty((p.T, p.H // 32), dtype=torch.uint8, device=dev)
+    q.mx_block_quantize(xd, codes, e8)
+    out_n = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    ssq_n = torch.full((p.T, 2), float("nan"), dtype=torch.float32, device=dev)
+    ws_n = torch.empty(q.qkv_mx_workspace_bytes(p.T, p.H, p.I), dtype=torch.uint8, device=dev)
+    q.qkv_mx_project(codes, e8, wp, out_n, ssq=ssq_n, workspace=ws_n, **kw)
+    img, eimg = _image(q, p.T, p.H, dev), _exp_image(q, p.T, p.H, dev)
+    q.mx_block_quantize_staged(xd, img, eimg)
+    out_s = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    ssq_s = torch.full((p.T, 2), float("nan"), dtype=torch.float32, device=dev)
+    ws_s = torch.empty(q.qkv_staged_workspace_bytes(p.T, p.I), dtype=torch.uint8, device=dev)
+    q.qkv_mx_project_staged(img, eimg, wp, out_s, T=p.T, ssq=ssq_s, workspace=ws_s, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out_s.view(torch.int16), out_n.view(torch.int16)), f"{name}: outputs differ"
+    assert torch.equal(ssq_s, ssq_n), f"{name}: sums differ"
+    got = G.bf16_host(out_s)
+    if layout:
+        got = oracle.nbsd_to_bsd(got)
+    G.check_close(got, X, f"{name} X")
+    G.check_ssq(ssq_s.cpu().numpy(), ssq_ref, f"{name} ssq")
