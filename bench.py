@@ -138,7 +138,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=5, choices=[2, 3, 5])
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5],
+                    help="5: producer + self-attention projection at the full video shape (the "
+                         "headline); 3 / 2 / 1: the self-attention projection at T = 75600 / "
+                         "4096 / 128 (activations quantised once, outside the step); 4: the "
+                         "cross-attention's three separate projections (Q from 75600 latent "
+                         "tokens, K and V from 512 context tokens) with the norm on Q and K")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the MFMA-rate and copy-bandwidth calibration after the timed steps")
@@ -211,6 +216,12 @@ def algorithmic_bytes(p, producer: bool, mx: bool = False):
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def synth_configs_separate(cid: int) -> bool:
+    """Whether workload `cid` is made of several separate projection calls."""
+    import synth
+    return len(synth.CONFIGS[cid].calls) > 1
 
 
 def run_gpu(args):
@@ -409,6 +420,108 @@ def measure_ceilings():
     return res
 
 
+def run_gpu_separate(args):
+    """The cross-attention workload: three single-segment projections (num_kv_heads = 0) on
+    staged ROW_MX activations, each followed by its norm pass where the call norms (no RoPE).
+    The activations are quantised once, outside the timed step."""
+    import torch
+
+    import rope_mxfp8_qkv_amd as q
+    import synth
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[args.config]
+    stream = torch.cuda.current_stream()
+    t0 = time.time()
+    calls = []
+    for p in cfg.calls:
+        c = {"p": p}
+        x = torch.from_numpy(synth.activation(p)).to(dev)
+        c["img"] = torch.empty(q.qkv_act_image_bytes(p.T, p.H), dtype=torch.uint8, device=dev)
+        c["sc"] = torch.empty((p.T,), dtype=torch.float32, device=dev)
+        q.row_quantize_staged(x, c["img"], c["sc"])
+        del x
+        w = torch.from_numpy(synth.weight(p)).to(dev)
+        codes = torch.empty((p.H // 4, p.I, 4), dtype=torch.uint8, device=dev)
+        e8 = torch.empty((p.H // 32, p.I), dtype=torch.uint8, device=dev)
+        q.mx_weight_quantize(w, codes, e8)
+        c["wp"] = q.prepare_weight(codes, e8, p.H, p.I)
+        del w, codes, e8
+        bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        c["bias"] = bf(synth.bias_bf16(p))
+        c["gq"] = bf(synth.gamma_bf16(p, "q"))
+        c["out"] = torch.empty((p.T, p.I), dtype=torch.bfloat16, device=dev)
+        c["flags"] = (q.NORM_Q if p.norm_q else 0) | (q.FUSED_ROPE if p.rope else 0)
+        c["ssq"] = torch.empty((p.T, 2), dtype=torch.float32, device=dev) if c["flags"] & q.NORM_Q else None
+        c["ws"] = torch.empty(q.qkv_staged_workspace_bytes(p.T, p.I), dtype=torch.uint8, device=dev)
+        calls.append(c)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f} s")
+
+    def step(ev=None):
+        for i, c in enumerate(calls):
+            p = c["p"]
+            if ev:
+                ev[2 * i].record(stream)
+            q.qkv_rowmx_project_staged(c["img"], c["sc"], c["wp"], c["out"], H=p.H,
+                                       num_heads=p.num_heads, num_kv_heads=p.num_kv_heads,
+                                       head_dim=p.head_dim, bias=c["bias"], ssq=c["ssq"],
+                                       workspace=c["ws"])
+            if ev:
+                ev[2 * i + 1].record(stream)
+            if c["flags"]:
+                q.qk_norm_rope_apply(c["out"], num_heads=p.num_heads, num_kv_heads=p.num_kv_heads,
+                                     head_dim=p.head_dim, eps=1e-6, flags=c["flags"], ssq=c["ssq"],
+                                     q_gamma=c["gq"])
+        if ev:
+            ev[-1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    n_ev = 2 * len(calls) + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = [c["p"].name for c in calls]
+    proj = np.array([[e[2 * i].elapsed_time(e[2 * i + 1]) for i in range(len(calls))] for e in evs])
+    after = np.array([[e[2 * i + 1].elapsed_time(e[2 * i + 2]) for i in range(len(calls))] for e in evs])
+    ms_step = wall * 1e3 / args.steps
+    flops = [2.0 * c["p"].T * c["p"].H * c["p"].I for c in calls]
+    stages, rates = {}, {}
+    for i, c in enumerate(calls):
+        p = c["p"]
+        pm = float(proj[:, i].mean())
+        stages[f"{names[i]}_projection"] = pm
+        rates[f"{names[i]}_projection_tflops"] = flops[i] / (pm * 1e-3) / 1e12
+        if c["flags"]:
+            nm = float(after[:, i].mean())
+            nbytes = 4 * p.T * p.Iq + 8 * p.T + 2 * p.Iq
+            stages[f"{names[i]}_norm"] = nm
+            rates[f"{names[i]}_norm_gbs"] = nbytes / (nm * 1e-3) / 1e9
+    big = int(np.argmax(flops))
+    ach = rates[f"{names[big]}_projection_tflops"]
+    line = {
+        "metric": METRIC, "value": sum(flops) / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp8 (e4m3 x e4m3 -> fp32 MFMA), fp32 norm, bf16 I/O", "data": "synthetic",
+        "config": {"workload": "cross-attention: separate Q, K, V projections on staged ROW_MX "
+                               "activations + across-heads norm on Q and K (no RoPE)",
+                   "calls": [{"name": c["p"].name, "T": c["p"].T, "H": c["p"].H, "I": c["p"].I}
+                             for c in calls],
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": f"qkv_rowmx_project_staged ({names[big]} call)", "bound": "mfma",
+                     "achieved": ach, "peak": PEAK_MXFP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ach / PEAK_MXFP8_TFLOPS, "traffic": None},
+        "stages": {"ms": stages, **rates},
+        "ceilings": None, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(cid, rows_n):
     """The oracle, as it stands, on the first ``rows_n`` tokens of the same workload."""
     import oracle
@@ -461,6 +574,9 @@ def main():
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
                                    "(multi-GPU sharding is described in DESIGN.md, not built)"}))
         sys.exit(2)
+    if synth_configs_separate(args.config):
+        run_gpu_separate(args)
+        return
     r = run_gpu(args)
     p = r["p"]
     log(f"gpu: {r['ms_per_step']:.3f} ms/step, stages {r['stage_ms']}")
