@@ -162,6 +162,10 @@ def parse():
                     help="per-head qk-norm (RMS_NORM / LAYER_NORM) + RoPE fused into the projection's "
                          "epilogue instead of the across-heads norm pass (ROW_MX activations)")
     ap.add_argument("--cpu-rows", type=int, default=8192)
+    ap.add_argument("--flush-mall", type=int, default=0, metavar="BYTES",
+                    help="write a BYTES-byte scratch buffer between timed steps (outside the step's "
+                         "events) so that no step finds the previous step's data in the 256 MB "
+                         "last-level cache; ms_per_step is then the mean of the steps' own events")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
@@ -222,6 +226,12 @@ def synth_configs_separate(cid: int) -> bool:
     """Whether workload `cid` is made of several separate projection calls."""
     import synth
     return len(synth.CONFIGS[cid].calls) > 1
+
+
+def stage_stats(ms, names):
+    """Median and minimum over the timed steps of each stage's event time (ms)."""
+    return {n: {"median": float(np.median(ms[:, i])), "min": float(ms[:, i].min())}
+            for i, n in enumerate(names)}
 
 
 def run_gpu(args):
@@ -333,21 +343,28 @@ def run_gpu(args):
         if ev:
             ev[3].record(stream)
 
-    for _ in range(args.warmup):
+    flush = (torch.empty(args.flush_mall // 4, dtype=torch.float32, device=dev)
+             if args.flush_mall else None)
+    for k in range(args.warmup):
+        if flush is not None:
+            flush.fill_(float(k))
         step()
     torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
+    log(f"warmup done ({args.warmup} steps); timing {args.steps} steps"
+        + (f", {args.flush_mall} bytes written between steps" if flush is not None else ""))
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
+        if flush is not None:
+            flush.fill_(float(k))
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     stage = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
                       for e in evs])
     ms = stage.mean(axis=0)          # producer, projection (+ sum reduce), norm/rope
-    ms_step = wall * 1e3 / args.steps
+    ms_step = (float(stage.sum(axis=1).mean()) if flush is not None else wall * 1e3 / args.steps)
     flops = 2.0 * T * H * I
     nbytes = algorithmic_bytes(p, inp["producer"], mx)
     proj_tflops = flops / (ms[1] * 1e-3) / 1e12
@@ -356,6 +373,7 @@ def run_gpu(args):
         "value": flops / (ms_step * 1e-3) / 1e12,
         "stage_ms": {"producer": float(ms[0]), "projection": float(ms[1]),
                      "norm_rope": float(ms[2])},
+        "stage_stats": stage_stats(stage, ["producer", "projection", "norm_rope"]),
         "projection_tflops": proj_tflops,
         "norm_rope_gbs": None if hn else nbytes["norm_rope"] / (ms[2] * 1e-3) / 1e9,
         "producer_gbs": (nbytes["producer"] / (ms[0] * 1e-3) / 1e9) if inp["producer"] else None,
@@ -491,6 +509,8 @@ def run_gpu_separate(args):
     ms_step = wall * 1e3 / args.steps
     flops = [2.0 * c["p"].T * c["p"].H * c["p"].I for c in calls]
     stages, rates = {}, {}
+    stats = {**stage_stats(proj, [f"{n}_projection" for n in names]),
+             **stage_stats(after, [f"{n}_after_projection" for n in names])}
     for i, c in enumerate(calls):
         p = c["p"]
         pm = float(proj[:, i].mean())
@@ -516,7 +536,7 @@ def run_gpu_separate(args):
         "roofline": {"kernel": f"qkv_rowmx_project_staged ({names[big]} call)", "bound": "mfma",
                      "achieved": ach, "peak": PEAK_MXFP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": ach / PEAK_MXFP8_TFLOPS, "traffic": None},
-        "stages": {"ms": stages, **rates},
+        "stages": {"ms": stages, "ms_median_min": stats, **rates},
         "ceilings": None, "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
@@ -619,6 +639,7 @@ def main():
             "num_kv_heads": p.num_kv_heads, "head_dim": p.head_dim,
             "grid": list(p.grid) if p.grid else None, "layout": args.layout.upper().replace("NBSD", "NBSd"),
             "parallelism": "single GPU",
+            "mall_flush_bytes_between_steps": args.flush_mall,
         },
         "roofline": {
             "kernel": ("qkv_mx_project_staged (counter reset + project_kernel + ssq_reduce)"
@@ -641,6 +662,7 @@ def main():
         },
         "stages": {
             "ms": r["stage_ms"],
+            "ms_median_min": r["stage_stats"],
             "projection_tflops": r["projection_tflops"],
             "norm_rope_gbs": r["norm_rope_gbs"],
             "norm_rope_hbm_frac": (r["norm_rope_gbs"] / PEAK_HBM_GBS) if r["norm_rope_gbs"] else None,
