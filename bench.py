@@ -389,11 +389,13 @@ def run_gpu(args):
     return res
 
 
-def measure_ceilings():
+def measure_ceilings(p=None):
     """What this GPU sustains outside the kernels, measured in the same run (context for the
     roofline fractions, which divide by the published peaks): the scaled FP8 MFMA issue rate on
     register operands (random E4M3 codes, as the workload's, and zeros) with the clock the chip
-    held meanwhile, and the bandwidth of a plain device-to-device copy (read + write bytes)."""
+    held meanwhile, the bandwidth of a plain device-to-device copy (read + write bytes) and, for
+    the projection's shape ``p``, torch's FP8 GEMM with one scale per tensor (the vendor
+    library's kernel; no block scales, no sum of squares) on random E4M3 operands."""
     import torch
     import rope_mxfp8_qkv_amd as q
     dev = torch.device("cuda:0")
@@ -435,7 +437,39 @@ def measure_ceilings():
     res["mfma_probe"] = (f"{blocks} blocks x 4 wavefronts x {iters} x 16 "
                          "V_MFMA_SCALE_F32_32X32X64_F8F6F4 on register operands, best of 4")
     res["copy"] = f"torch device copy of {n} bytes, median of 5"
+    del src, dst
+    if p is not None:
+        res.update(library_gemm(p.T, p.H, p.I))
     return res
+
+
+def library_gemm(M, K, N):
+    """torch._scaled_mm (tensor-wise scales) at [M, K] x [K, N] -> bf16: codes spread over the
+    E4M3 range as the workload's (|x| up to 448), median of 10 timed calls after 3 warm-ups."""
+    import torch
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    a = torch.randn(M, K, device=dev, generator=g).mul_(100.0).clamp_(-448, 448).to(torch.float8_e4m3fn)
+    b = torch.randn(N, K, device=dev, generator=g).mul_(150.0).clamp_(-448, 448).to(torch.float8_e4m3fn)
+    sa = torch.tensor(1.0 / 100, device=dev)
+    sb = torch.tensor(1.0 / 150, device=dev)
+    stream = torch.cuda.current_stream()
+    ts = []
+    for i in range(13):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        out = torch._scaled_mm(a, b.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 3:
+            ts.append(e0.elapsed_time(e1))
+        del out
+    ms = float(np.median(ts))
+    return {"library_fp8_gemm_ms": ms,
+            "library_fp8_gemm_tflops": 2.0 * M * K * N / (ms * 1e-3) / 1e12,
+            "library_fp8_gemm": (f"torch._scaled_mm, tensor-wise scales, [{M}, {K}] x [{K}, {N}] "
+                                 "e4m3 -> bf16, median of 10")}
 
 
 def run_gpu_separate(args):
@@ -600,9 +634,10 @@ def main():
     r = run_gpu(args)
     p = r["p"]
     log(f"gpu: {r['ms_per_step']:.3f} ms/step, stages {r['stage_ms']}")
-    ceil = None if args.no_ceilings else measure_ceilings()
+    ceil = None if args.no_ceilings else measure_ceilings(p)
     if ceil:
         ceil["projection_frac_of_mfma_random"] = r["projection_tflops"] / ceil["mfma_random_operands_tflops"]
+        ceil["projection_vs_library_fp8_gemm"] = r["projection_tflops"] / ceil["library_fp8_gemm_tflops"]
         if r["norm_rope_gbs"]:
             ceil["norm_rope_frac_of_copy"] = r["norm_rope_gbs"] / ceil["hbm_copy_gbs"]
         if r["producer_gbs"]:
