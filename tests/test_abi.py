@@ -135,6 +135,8 @@ def test_producer_and_weight_validation():
     assert L.rmsnorm_mx_quantize(P, None, P, 1e-6, 4, 250, 0, None, P, None) == 2
     assert L.rmsnorm_mx_quantize(P, None, P, 1e-6, 4, 256, 257, None, P, None) == 2
     assert L.rmsnorm_mx_quantize(P, None, P, 1e-6, 4, 32768, 0, None, P, None) == 6
+    assert L.rmsnorm_mx_quantize(P, None, P, 1e-6, 4, 16384 + 32, 0, None, P, None) == 6  # widest: 16384
+    assert L.row_quantize_packed(P, 0, 4, 16384 + 32, P, None) == 6
     assert L.rmsnorm_mx_quantize(None, None, P, 1e-6, 4, 256, 0, None, P, None) == 1
     assert L.row_quantize_packed(P, 5, 4, 256, P, None) == 4
     assert L.row_quantize_packed(P, 0, 4, 96 + 8, P, None) == 2
@@ -171,6 +173,7 @@ def test_staged_path_validation():
     assert L.row_quantize_staged(P, 0, 4, 250, P, 1 << 20, P, None) == 2
     assert L.row_quantize_staged(P, 0, 4, 256, P, 100, P, None) == 2
     assert L.row_quantize_staged(P, 0, 4, 32768, P, 1 << 30, P, None) == 6
+    assert L.row_quantize_staged(P, 0, 4, 16384 + 32, P, 1 << 30, P, None) == 6
     assert L.row_quantize_staged(P, 0, 4, 256, P + 8, 1 << 20, P, None) == 3
     # (hidden, residual, gamma, eps, T, H, Hu, residual_out, image, image_bytes, row_scale, s)
     assert L.rmsnorm_mx_quantize_staged(P, P, P, 1e-6, 4, 256, 0, None, P, 1 << 20, P, None) == 4
@@ -248,6 +251,7 @@ def test_mx_path_validation():
     assert L.mx_block_quantize(P, 2, 4, 256, P, P, None) == 4
     assert L.mx_block_quantize(P, 0, 4, 256, P + 4, P, None) == 3
     assert L.mx_block_quantize(P, 0, 4, 32768, P, P, None) == 6
+    assert L.mx_block_quantize(P, 0, 4, 16384 + 32, P, P, None) == 6
     assert L.rmsnorm_mx_block_quantize(P, P, P, 1e-6, 4, 256, 0, None, P, P, None, None) == 4
     assert L.rmsnorm_mx_block_quantize(P, None, P, 1e-6, 4, 256, 0, None, P, P, P + 8, None) == 3
     assert L.rmsnorm_mx_block_quantize(P, None, P, -1.0, 4, 256, 0, None, P, P, None, None) == 4
