@@ -162,6 +162,9 @@ def parse():
                     help="per-head qk-norm (RMS_NORM / LAYER_NORM) + RoPE fused into the projection's "
                          "epilogue instead of the across-heads norm pass (ROW_MX activations)")
     ap.add_argument("--cpu-rows", type=int, default=8192)
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one step into a HIP graph and time --steps replays of it "
+                         "(stages.graph_ms_per_step)")
     ap.add_argument("--flush-mall", type=int, default=0, metavar="BYTES",
                     help="write a BYTES-byte scratch buffer between timed steps (outside the step's "
                          "events) so that no step finds the previous step's data in the 256 MB "
@@ -364,6 +367,26 @@ def run_gpu(args):
     stage = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
                       for e in evs])
     ms = stage.mean(axis=0)          # producer, projection (+ sum reduce), norm/rope
+    graph_ms = None
+    if args.graph:                   # the same step as one HIP graph, replayed back to back
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+        log(f"graph replays: {graph_ms:.4f} ms/step")
     ms_step = (float(stage.sum(axis=1).mean()) if flush is not None else wall * 1e3 / args.steps)
     flops = 2.0 * T * H * I
     nbytes = algorithmic_bytes(p, inp["producer"], mx)
@@ -374,6 +397,7 @@ def run_gpu(args):
         "stage_ms": {"producer": float(ms[0]), "projection": float(ms[1]),
                      "norm_rope": float(ms[2])},
         "stage_stats": stage_stats(stage, ["producer", "projection", "norm_rope"]),
+        "graph_ms_per_step": graph_ms,
         "projection_tflops": proj_tflops,
         "norm_rope_gbs": None if hn else nbytes["norm_rope"] / (ms[2] * 1e-3) / 1e9,
         "producer_gbs": (nbytes["producer"] / (ms[0] * 1e-3) / 1e9) if inp["producer"] else None,
@@ -698,6 +722,7 @@ def main():
         "stages": {
             "ms": r["stage_ms"],
             "ms_median_min": r["stage_stats"],
+            "graph_ms_per_step": r["graph_ms_per_step"],
             "projection_tflops": r["projection_tflops"],
             "norm_rope_gbs": r["norm_rope_gbs"],
             "norm_rope_hbm_frac": (r["norm_rope_gbs"] / PEAK_HBM_GBS) if r["norm_rope_gbs"] else None,
