@@ -17,6 +17,7 @@ the library launches on, averaged over the timed steps.  ``cpu_baseline`` times 
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -606,10 +607,11 @@ def cpu_baseline(cid, rows_n):
     import synth
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
+        blas_pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in blas_pools] or [1])
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in blas_pools) or None
     except Exception:                                        # pragma: no cover
-        threads = 1
+        threads, blas = 1, None
     cfg = synth.CONFIGS[cid]
     p = cfg.calls[0]
     rows = np.arange(rows_n)
@@ -626,16 +628,24 @@ def cpu_baseline(cid, rows_n):
         _, packed, _ = oracle.rmsnorm_rowmx(hid, res, gam, 1e-6)
     else:
         packed = oracle.rowmx_quantize(x)
+    t1 = time.perf_counter()
     codes, sA = oracle.rowmx_unpack(packed, p.H)
     X, ssq = oracle.project(codes, sA, wc, we, None, bias, num_heads=p.num_heads,
                             num_kv_heads=p.num_kv_heads, head_dim=p.head_dim)
     xb = oracle.f64_to_bf16(X)
+    t2 = time.perf_counter()
     oracle.norm_rope(xb, ssq, gq, gk, cos, sin, num_heads=p.num_heads,
                      num_kv_heads=p.num_kv_heads, head_dim=p.head_dim, eps=1e-6, flags=7)
-    dt = time.perf_counter() - t0
+    t3 = time.perf_counter()
+    dt = t3 - t0
     flops = 2.0 * rows_n * p.H * p.I
+    nb = algorithmic_bytes(dataclasses.replace(p, T=rows_n), cfg.producer)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "blas": blas,
+            "stages": {"producer_or_quantise_s": t1 - t0,
+                       "producer_gbs": (nb["producer"] / (t1 - t0) / 1e9) if cfg.producer else None,
+                       "projection_s": t2 - t1, "projection_tflops": flops / (t2 - t1) / 1e12,
+                       "norm_rope_s": t3 - t2, "norm_rope_gbs": nb["norm_rope"] / (t3 - t2) / 1e9},
             "sample": f"first {rows_n} of {p.T} tokens, whole step (producer/quantise, "
                       f"fp64 projection incl. weight decode, norm+RoPE); {dt:.1f} s"}
 
