@@ -210,9 +210,22 @@ qkvmx_status rmsnorm_mx_block_quantize_staged(const uint16_t* hidden, const uint
  * ------------------------------------------------------------------------------------------ */
 
 /* Workspace bytes qkv_rowmx_project needs for a [T, H] x [H, I] call: the activation codes
- * re-laid in the kernel's LDS stage images (about T * H bytes) plus per-tile sums of squares.
- * 0 for invalid sizes. */
+ * re-laid in the kernel's LDS stage images (about T * H bytes) plus per-tile sums of squares
+ * and, for calls with few output tiles (see qkvmx_projection_k_chunks), k fp32 [T, I] planes
+ * of the split contraction, k = min(3, 256 / tiles), tiles = ceil(T / 256) * ceil(I / 256)
+ * <= 128.  0 for invalid sizes. */
 size_t qkvmx_workspace_bytes(int64_t T, int64_t H, int64_t I);
+
+/* Number of K chunks the projections (qkv_rowmx_project[_staged], qkv_mx_project[_staged])
+ * cut a [T, H] x [H, I] call into.  A call with at most 128 output tiles of 256 x 256 leaves
+ * most compute units idle, so its 256-byte K supersteps are split into up to
+ * min(3, 256 / tiles) chunks of ceil(supersteps / that) supersteps; each (tile, chunk) unit
+ * writes its fp32 partial sums to a plane of the workspace, and a per-token pass adds the
+ * planes in chunk order and applies the epilogue (scales, bias, bf16 rounding, sums of
+ * squares; BSD or NBSd store).  The result is the same function of the inputs, accumulated in
+ * a different fp32 order, and identical for both layouts.  1 = no split; 0 for invalid sizes
+ * or layout.  Host only. */
+int32_t qkvmx_projection_k_chunks(int64_t T, int64_t H, int64_t I, int32_t layout);
 
 /* out[t, i] = bf16_RNE( a_scale[t] * c[i] * sum_h dec(a[t, h]) * dec(W[h, i]) * 2^(E[h/32, i]-127)
  *                       + bias[i] )
@@ -240,8 +253,9 @@ qkvmx_status qkv_rowmx_project(const uint8_t* a_codes, int64_t a_row_stride,
                                uint16_t* out, float* ssq, void* workspace, size_t ws_bytes,
                                hipStream_t stream);
 
-/* Workspace bytes qkv_rowmx_project_staged needs: the per-tile sums of squares and the tile
- * counters (no activation re-layout).  0 for invalid sizes. */
+/* Workspace bytes qkv_rowmx_project_staged (and qkv_mx_project_staged) needs: the per-tile
+ * sums of squares, the tile counters (no activation re-layout) and, for calls with few tiles,
+ * the split contraction's planes (as for qkvmx_workspace_bytes).  0 for invalid sizes. */
 size_t qkv_staged_workspace_bytes(int64_t T, int64_t I);
 
 /* qkv_rowmx_project on staged activations (act_image, row_scale written by
@@ -293,7 +307,8 @@ qkvmx_status qkv_rowmx_project_headnorm(const uint8_t* a_codes, int64_t a_row_st
 
 /* Workspace bytes qkv_mx_project needs for a [T, H] x [H, I] call: the activation codes and
  * their exponents re-laid in the kernel's LDS stage images (about T * H * 33 / 32 bytes) plus
- * per-tile sums of squares.  0 for invalid sizes. */
+ * per-tile sums of squares and, for calls with few tiles, the split contraction's planes (as
+ * for qkvmx_workspace_bytes).  0 for invalid sizes. */
 size_t qkv_mx_workspace_bytes(int64_t T, int64_t H, int64_t I);
 
 /* Pass 1 on MX block-32 activations ([RMSNORM-MX] qmx_output_dtype feeding [QKV-CTE]'s

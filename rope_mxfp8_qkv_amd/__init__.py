@@ -25,7 +25,7 @@ __all__ = [
     "HEAD_LAYER_NORM", "qkv_act_image_bytes", "row_quantize_staged", "rmsnorm_mx_quantize_staged",
     "qkv_staged_workspace_bytes", "qkv_rowmx_project_staged", "mfma_rate_probe",
     "qkv_act_exp_image_bytes", "mx_block_quantize_staged", "rmsnorm_mx_block_quantize_staged",
-    "qkv_mx_project_staged",
+    "qkv_mx_project_staged", "projection_k_chunks",
 ]
 
 
@@ -248,6 +248,11 @@ def qkv_rowmx_project(packed_a, w_packed, out, *, H: int, num_heads: int, num_kv
 
 def qkv_staged_workspace_bytes(T: int, I: int) -> int:
     return int(lib().qkv_staged_workspace_bytes(T, I))
+
+
+def projection_k_chunks(T: int, H: int, I: int, layout: int = LAYOUT_BSD) -> int:
+    """K chunks the projections split a [T, H] x [H, I] call into (1: no split)."""
+    return int(lib().qkvmx_projection_k_chunks(T, H, I, layout))
 
 
 def qkv_rowmx_project_staged(act_image, row_scale, w_packed, out, *, H: int, num_heads: int,

@@ -52,6 +52,7 @@ SIGNATURES = {
     "rmsnorm_mx_quantize_staged": (c_i32, [c_vp, c_vp, c_vp, c_f, c_i64, c_i64, c_i64, c_vp, c_vp,
                                            c_sz, c_vp, c_vp]),
     "qkv_staged_workspace_bytes": (c_sz, [c_i64, c_i64]),
+    "qkvmx_projection_k_chunks": (c_i32, [c_i64, c_i64, c_i64, c_i32]),
     "qkv_rowmx_project_staged": (c_i32, [c_vp, c_sz, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i32,
                                          c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "qkv_act_exp_image_bytes": (c_sz, [c_i64, c_i64]),
@@ -83,6 +84,13 @@ def lib():
         if not os.path.exists(_LIB_PATH):
             raise QkvmxError(f"{_LIB_PATH} is missing: build it with "
                              "`python -m rope_mxfp8_qkv_amd.build` (no fallback path exists)")
+        # torch (which brings its own HIP runtime) is loaded before the library: loaded first,
+        # the library's HIP calls later failed in the same process ("no ROCm-capable device")
+        # once torch had initialised the GPU
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(_LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             f = getattr(L, name)

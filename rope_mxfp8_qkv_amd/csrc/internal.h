@@ -49,6 +49,43 @@ inline size_t packed_total_bytes(int64_t H, int64_t I) {
   return packed_zero_offset(H, I) + kZeroPage;
 }
 inline int64_t ssq_partials(int64_t I) { return ceil_div(I, kTileN) * (kTileN / kPartialN); }
+// Split contraction for calls with few output tiles (at most kSplitMaxTiles 256 x 256 tiles,
+// e.g. a 512-token context projection): the K range is cut into up to kMaxSplit chunks (and
+// at most kSplitUnits units in all), each (tile, chunk) unit stores its fp32 partial tile into
+// its own [T, I] plane, and a per-token pass sums the planes and applies the epilogue.  Each
+// unit streams 512 bytes of operands per K-byte but writes a 256 KiB plane tile whatever its
+// K range, so deeper splits trade idle compute units for plane traffic: on the 512 x 5120 ->
+// 5120 context calls 2, 3, 4 and 5 chunks measured 58.9, 56.0, 59.1 and 63.0 us against
+// 66.1 us unsplit.  The factor depends on T and I only, so the workspace queries can size the
+// planes.
+constexpr int64_t kSplitMaxTiles = 128;
+constexpr int64_t kSplitUnits = 256;
+constexpr int64_t kMaxSplit = 3;
+inline int split_factor(int64_t T, int64_t I) {
+  const int64_t tiles = ceil_div(T, kTileM) * ceil_div(I, kTileN);
+  if (tiles > kSplitMaxTiles) return 1;
+  const int64_t s = kSplitUnits / tiles;
+  return (int)(s < kMaxSplit ? s : kMaxSplit);
+}
+inline size_t split_planes_bytes(int64_t T, int64_t I) {
+  const int s = split_factor(T, I);
+  return s > 1 ? (size_t)s * (size_t)T * (size_t)I * sizeof(float) : 0;
+}
+// The K chunks a BSD call actually uses: ceil(supersteps / factor) supersteps each, so the
+// last chunk may be shorter; {1, all stages} when the call does not split.
+struct SplitPlan {
+  int chunks;
+  int stages_per_chunk;
+};
+inline SplitPlan split_plan(int64_t T, int64_t H, int64_t I) {
+  const int64_t nsup = ceil_div(H, kSuperK);
+  const int sf = split_factor(T, I);
+  const SplitPlan whole{1, (int)(4 * nsup)};
+  if (sf < 2) return whole;
+  const int64_t chunk = ceil_div(nsup, sf);
+  const int used = (int)ceil_div(nsup, chunk);
+  return used < 2 ? whole : SplitPlan{used, (int)(4 * chunk)};
+}
 // Projection workspace: the activation codes re-laid as stage images [MT][KS][16 KiB]
 // (MT = ceil(T / 256) token tiles), then the sum-of-squares partials [P][T][2] fp32, then a
 // 256-byte block holding the per-XCD tile counters of the projection's tile scheduler.
@@ -62,8 +99,9 @@ constexpr size_t kCounterBytes = 256;
 inline size_t counters_offset(int64_t T, int64_t H, int64_t I) {
   return (act_image_bytes(T, H) + partials_bytes(T, I) + 255) / 256 * 256;
 }
+// the split-contraction planes (when the call has few tiles) follow the counter block
 inline size_t workspace_total_bytes(int64_t T, int64_t H, int64_t I) {
-  return counters_offset(T, H, I) + kCounterBytes;
+  return counters_offset(T, H, I) + kCounterBytes + split_planes_bytes(T, I);
 }
 // MX-activation projection workspace: the activation code stage images (as above), their
 // exponents re-laid per (token tile, superstep) as [256][2] dwords, the sum-of-squares
@@ -79,17 +117,17 @@ inline size_t mx_counters_offset(int64_t T, int64_t H, int64_t I) {
   return (mx_partials_offset(T, H) + partials_bytes(T, I) + 255) / 256 * 256;
 }
 inline size_t mx_workspace_total_bytes(int64_t T, int64_t H, int64_t I) {
-  return mx_counters_offset(T, H, I) + kCounterBytes;
+  return mx_counters_offset(T, H, I) + kCounterBytes + split_planes_bytes(T, I);
 }
 
 // Projection on staged activations (codes already in the stage-image layout, written by a
-// staged producer): the workspace holds only the sum-of-squares partials [P][T][2] fp32 and,
-// after them, the 256-byte counter block.
+// staged producer): the workspace holds only the sum-of-squares partials [P][T][2] fp32,
+// after them the 256-byte counter block, then the split-contraction planes (few tiles only).
 inline size_t staged_counters_offset(int64_t T, int64_t I) {
   return (partials_bytes(T, I) + 255) / 256 * 256;
 }
 inline size_t staged_workspace_total_bytes(int64_t T, int64_t I) {
-  return staged_counters_offset(T, I) + kCounterBytes;
+  return staged_counters_offset(T, I) + kCounterBytes + split_planes_bytes(T, I);
 }
 
 hipError_t launch_mx_weight_quantize(const float* w, int64_t H, int64_t I, uint8_t* codes,

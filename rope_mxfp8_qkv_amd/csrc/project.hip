@@ -23,7 +23,8 @@ hipError_t launch_project(const uint8_t* a_codes, int64_t a_stride, const uint8_
                      a.ctr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_core<false>(a, chan_scale, bias, nbsd, ssq, s);
+  return launch_core<false>(a, chan_scale, bias, nbsd, ssq, s,
+                            ws + counters_offset(T, H, I) + kCounterBytes);
 }
 
 hipError_t launch_project_staged(const uint8_t* img, const float* row_scale,
@@ -39,7 +40,8 @@ hipError_t launch_project_staged(const uint8_t* img, const float* row_scale,
   hipLaunchKernelGGL(reset_counters_kernel, dim3(1), dim3(64), 0, s, a.ctr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_core<false>(a, chan_scale, bias, nbsd, ssq, s);
+  return launch_core<false>(a, chan_scale, bias, nbsd, ssq, s,
+                            ws + staged_counters_offset(T, I) + kCounterBytes);
 }
 
 }  // namespace qkvmx

@@ -96,6 +96,12 @@ struct ProjectArgs {
   float h_eps;
   const float* cos_tab;
   const float* sin_tab;
+  // split contraction: work unit v is tile v / ksplit over K-stages [kz * ks_chunk,
+  // min(KS, (kz + 1) * ks_chunk)), kz = v % ksplit; its fp32 accumulators go to plane kz of
+  // part ([ksplit][T][I]), summed by split_reduce_kernel
+  int ksplit;
+  int ks_chunk;
+  float* part;
 };
 
 __device__ __forceinline__ int lds_off(int row, int chunk) {
@@ -165,13 +171,14 @@ constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 // kGroupM token tiles, walked channel tile by channel tile.
 struct Tile {
   int tm, tn;
+  int kz;          // K chunk (split contraction; 0 otherwise)
 };
 __device__ __forceinline__ Tile decode_tile(int tile, int tiles_m, int tiles_n) {
   const int group = tile / (kGroupM * tiles_n);
   const int first_m = group * kGroupM;
   const int gm = min(tiles_m - first_m, kGroupM);
   const int in_group = tile % (kGroupM * tiles_n);
-  return Tile{first_m + in_group % gm, in_group / gm};
+  return Tile{first_m + in_group % gm, in_group / gm, 0};
 }
 
 // kMx: MX block-32 activations (E4M3 rows with one E8M0 exponent per 32 elements).  Their
@@ -180,7 +187,10 @@ __device__ __forceinline__ Tile decode_tile(int tile, int tiles_m, int tiles_n) 
 // kHead: 0 = plain epilogue with the segment sums of squares; 1 / 2 = per-head RMS_NORM /
 // LAYER_NORM of the Q and K heads fused into the epilogue (head_dim 64 or 128, segments
 // multiples of 128 channels, no channel scale, no sums), with rotate-half RoPE when kRope.
-template <bool kChanScale, bool kBias, bool kNbsd, bool kMx, int kHead = 0, bool kRope = false>
+// kSplit: split contraction (work units = tile x K chunk); the epilogue only stores the raw
+// fp32 accumulators of its chunk (scales, bias, rounding and sums are split_reduce_kernel's).
+template <bool kChanScale, bool kBias, bool kNbsd, bool kMx, int kHead = 0, bool kRope = false,
+          bool kSplit = false>
 __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_w[kBufs][kStageImage];
   __shared__ __attribute__((aligned(16))) uint8_t lds_x[kBufs][kStageImage];
@@ -209,7 +219,13 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   // takes tiles from the other XCDs' ranges.  Thread 0 claims; the tile id reaches the block
   // through LDS.
   __shared__ int lds_tile[2];
-  const int ntiles = a.tiles_m * a.tiles_n;
+  const int ntiles = a.tiles_m * a.tiles_n * (kSplit ? a.ksplit : 1);
+  auto decode = [&](int v) -> Tile {
+    if (!kSplit) return decode_tile(v, a.tiles_m, a.tiles_n);
+    Tile u = decode_tile(v / a.ksplit, a.tiles_m, a.tiles_n);
+    u.kz = v % a.ksplit;
+    return u;
+  };
   const int per = ntiles / kXcds, rem = ntiles % kXcds;
   const int my_xcd = __builtin_amdgcn_s_getreg(kHwRegXccId) & (kXcds - 1);
   auto range_first = [&](int x) { return x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per; };
@@ -229,7 +245,7 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   __syncthreads();
   const int first_tile = __builtin_amdgcn_readfirstlane(lds_tile[0]);
   if (first_tile < 0) return;             // the whole block, nothing left
-  Tile t = decode_tile(first_tile, a.tiles_m, a.tiles_n);
+  Tile t = decode(first_tile);
 
   // ---- DMA sources of the current tile (wave-uniform bases, in SGPRs) ----
   // weight: wave w copies 1 KiB blocks 4 w .. 4 w + 3 of each 16 KiB stage image;
@@ -251,6 +267,13 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     sbase = a.w_scales + ((int64_t)u.tn * kTileN * 2) * 4 + wave * 512;
     xbase = a.x_img + ((int64_t)u.tm * a.KS) * kStageImage + wave * 4096;
     if (kMx) xsbase = a.x_scales + (int64_t)u.tm * (a.KS / 4) * xs_step + wave * 512;
+    if (kSplit) {                 // the unit's K chunk starts ks0 stages (ks0 / 4 supersteps) on
+      const int64_t ks0 = (int64_t)u.kz * a.ks_chunk;
+      wbase += ks0 * kStageImage;
+      xbase += ks0 * kStageImage;
+      sbase += (ks0 / 4) * s_step;
+      if (kMx) xsbase += (ks0 / 4) * xs_step;
+    }
   };
   set_sources(t);
 
@@ -732,6 +755,47 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     }
   };
 
+  // ---- split contraction: the unit's raw fp32 accumulators to its plane ----
+  // The next unit's stages 0-2 are requested first; then each lane stores its 64 accumulator
+  // quads (4 consecutive channels of one token, 16 bytes) through a buffer descriptor over
+  // the unit's [T, I] plane.  Quads outside [T, I] get an offset beyond the descriptor's range
+  // and the hardware drops them, so all 64 stores are issued unconditionally and the next
+  // unit's wait for all but the last kTailStores memory operations covers its DMAs.  The host
+  // keeps T * I * 4 < 2^31 for split calls.
+  auto split_store = [&](Tile u, bool more) __attribute__((always_inline)) {
+    if (more) {
+      issue(I0{}, 0);
+      issue(I1{}, 1);
+      issue(I2{}, 2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const int el = fresh_lane();
+    const int g = el >> 5, fr = el & 31;
+    const int64_t plane = a.T * a.I;
+    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+        a.part + (int64_t)u.kz * plane, (short)0,
+        (int)(uint32_t)min(plane * 4, (int64_t)0x7FFFFFFF), kBufferRsrcWord3);
+    const int64_t tok0 = (int64_t)u.tm * kTileM + wm * 128 + fr;
+    const int64_t ch0 = (int64_t)u.tn * kTileN + wn * 128 + g * 4;
+#pragma unroll
+    for (int tf = 0; tf < 4; ++tf) {
+      const int64_t tok = tok0 + tf * 32;
+#pragma unroll
+      for (int cf = 0; cf < 4; ++cf)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int64_t ch = ch0 + cf * 32 + rq * 8;
+          const uint32_t off =
+              (tok < a.T && ch < a.I) ? (uint32_t)((tok * a.I + ch) * 4) : kDropOffset;
+          const u32x4 v = {__float_as_uint(acc[cf][tf][rq * 4]),
+                           __float_as_uint(acc[cf][tf][rq * 4 + 1]),
+                           __float_as_uint(acc[cf][tf][rq * 4 + 2]),
+                           __float_as_uint(acc[cf][tf][rq * 4 + 3])};
+          __builtin_amdgcn_raw_buffer_store_b128(v, prs, (int)off, 0, 0);
+        }
+    }
+  };
+
   // ---- tile loop ----
   // Before the first tile: its stages 0-2 and epilogue operands requested and awaited.  Each
   // tile then: waits for everything in flight except the previous epilogue's last
@@ -744,7 +808,7 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   issue(I0{}, 0);
   issue(I1{}, 1);
   issue(I2{}, 2);
-  issue_ops(t, 0);
+  if (!kSplit) issue_ops(t, 0);
   wait_vm<0>();
   // the tile body, instantiated for operand buffer e = 0 and e = 1 (tiles alternate), so the
   // buffer index is a constant everywhere; returns whether another tile follows
@@ -766,8 +830,9 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     __syncthreads();
     // the trip count is re-read through an opaque copy each tile: a loop-invariant test hoisted
     // out of the tile loop would be kept in a register (or spilled) across the whole tile
-    int ks_opaque = KS;
+    int ks_opaque = kSplit ? min(a.ks_chunk, a.KS - t.kz * a.ks_chunk) : KS;
     asm volatile("" : "+s"(ks_opaque));
+    const int kend = kSplit ? ks_opaque : KS;     // K-stages of this unit
     // K-step 0 feeds zero accumulators to its MFMAs (no separate clearing of the 256 AGPRs)
     if (ks_opaque > 4) {
       step(I0{}, 0, Yes{}, W40{}, Z{});
@@ -781,17 +846,17 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
         step(I3{}, s + 3, Yes{}, W40{}, NZ{});
       }
       // last superstep: nothing left to request; the waits shrink with the groups in flight
-      step(I0{}, KS - 4, No{}, W20{}, NZ{});
+      step(I0{}, kend - 4, No{}, W20{}, NZ{});
     } else {
       step(I0{}, 0, No{}, W20{}, Z{});             // one superstep only
     }
-    step(I1{}, KS - 3, No{}, W0{}, NZ{});
+    step(I1{}, kend - 3, No{}, W0{}, NZ{});
     // every DMA has landed: draw the ticket for the next tile now (its latency passes during
     // the last two K-steps); the claim is published after them
     unsigned ticket;
     if (tid == 0) ticket = atomicAdd(&a.ctr[my_xcd], 1u);
-    step(I2{}, KS - 2, No{}, WN{}, NZ{});
-    step(I3{}, KS - 1, No{}, WN{}, NZ{});
+    step(I2{}, kend - 2, No{}, WN{}, NZ{});
+    step(I3{}, kend - 1, No{}, WN{}, NZ{});
     // pin the accumulators here: without this the compiler sinks the last superstep's MFMAs
     // (their results are only read by the epilogue) below the next tile's DMA requests
 #pragma unroll
@@ -806,11 +871,14 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     const int next_tile = __builtin_amdgcn_readfirstlane(lds_tile[e]);
     const bool more = next_tile >= 0;
     if (more) {
-      t = decode_tile(next_tile, a.tiles_m, a.tiles_n);
+      t = decode(next_tile);
       set_sources(t);
     }
     __builtin_amdgcn_sched_barrier(0);
-    epilogue(cur, e, more, t);
+    if constexpr (kSplit)
+      split_store(cur, more);
+    else
+      epilogue(cur, e, more, t);
     return more;
   };
   for (;;) {
@@ -905,19 +973,128 @@ __global__ void __launch_bounds__(64 * kReduceWaves) ssq_reduce_kernel(const flo
   }
 }
 
+// Split contraction, second pass: token t's row of every plane summed in plane order, then the
+// projection's epilogue on the sum: x = acc * a_scale * c + bias (fp32), bf16 out (BSD [T, I],
+// or NBSd [I / d, T, d] with kNbsd), and the sums of squares of the fp32 x over the Q and the
+// K segment.  One block per token, four channels per thread and step (I, d and the segment
+// bounds are multiples of 16, so a quad never straddles a head or a segment boundary); the
+// block's sums are combined in a fixed order.
+template <bool kRowScale, bool kChanScale, bool kBias, bool kNbsd>
+__global__ void __launch_bounds__(256) split_reduce_kernel(
+    const float* __restrict__ part, int S, int64_t T, int64_t I, int64_t Iq, int64_t Ik,
+    int64_t d, const uint8_t* __restrict__ a_scales, int64_t s_stride,
+    const float* __restrict__ chan, const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
+    float* __restrict__ ssq) {
+  __shared__ float2 red[4];
+  const int64_t t = blockIdx.x;
+  const float sa = kRowScale ? *reinterpret_cast<const float*>(a_scales + t * s_stride) : 1.0f;
+  const int64_t plane = T * I;
+  const float* const row = part + t * I;
+  float q = 0.f, k = 0.f;
+  for (int64_t c = (int64_t)threadIdx.x * 4; c < I; c += 1024) {
+    float4 acc = *reinterpret_cast<const float4*>(row + c);
+    for (int z = 1; z < S; ++z) {
+      const float4 p = *reinterpret_cast<const float4*>(row + z * plane + c);
+      acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+    }
+    const float av[4] = {acc.x, acc.y, acc.z, acc.w};
+    float bs[4] = {0.f, 0.f, 0.f, 0.f}, cs[4] = {1.f, 1.f, 1.f, 1.f};
+    if (kBias) {
+      const uint2 bw = *reinterpret_cast<const uint2*>(bias + c);
+      bs[0] = bf16_to_f32(bw.x & 0xFFFFu); bs[1] = bf16_to_f32(bw.x >> 16);
+      bs[2] = bf16_to_f32(bw.y & 0xFFFFu); bs[3] = bf16_to_f32(bw.y >> 16);
+    }
+    if (kChanScale) {
+      const float4 c4 = *reinterpret_cast<const float4*>(chan + c);
+      cs[0] = c4.x; cs[1] = c4.y; cs[2] = c4.z; cs[3] = c4.w;
+    }
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      x[i] = kChanScale ? av[i] * sa * cs[i] + bs[i] : fmaf(av[i], sa, bs[i]);
+    const float s2 = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+    if (c < Iq) q += s2;
+    else if (c < Iq + Ik) k += s2;
+    const u32x2_a8 o = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+    const int64_t at = kNbsd ? ((c / d) * T + t) * d + c % d : t * I + c;
+    *reinterpret_cast<u32x2_a8*>(out + at) = o;
+  }
+  if (ssq) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      q += __shfl_xor(q, off);
+      k += __shfl_xor(k, off);
+    }
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_float2(q, k);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float2 r = red[0];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        r.x += red[w].x;
+        r.y += red[w].y;
+      }
+      reinterpret_cast<float2*>(ssq)[t] = r;
+    }
+  }
+}
+
 }  // namespace
 
 namespace {
 
+// Split contraction (few tiles): project_kernel over tile x K-chunk units into the planes at
+// `planes`, then split_reduce_kernel.  Returns false (nothing launched) when the call has
+// enough tiles or its K range is a single superstep.
+template <bool kMx>
+bool launch_split(const ProjectArgs& a, bool chan, bool bias, bool nbsd, float* ssq,
+                  uint8_t* planes, int cus, hipStream_t s, hipError_t* err) {
+  const SplitPlan sp = split_plan(a.T, a.H, a.I);
+  if (sp.chunks < 2 || !planes) return false;
+  const int used = sp.chunks;
+  ProjectArgs b = a;
+  b.ksplit = used;
+  b.ks_chunk = sp.stages_per_chunk;
+  b.part = reinterpret_cast<float*>(planes);
+  const int64_t units = (int64_t)a.tiles_m * a.tiles_n * used;
+  const unsigned nblocks = (unsigned)std::min<int64_t>(units, std::max(cus, 1));
+  hipLaunchKernelGGL((project_kernel<false, false, false, kMx, 0, false, true>), dim3(nblocks),
+                     dim3(kThreads), 0, s, b);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) {
+    const dim3 rg((unsigned)a.T), rb(256);
+    const int variant = (chan ? 4 : 0) | (bias ? 2 : 0) | (nbsd ? 1 : 0);
+#define QKVMX_SPLIT_REDUCE(C, B, N)                                                          \
+  hipLaunchKernelGGL((split_reduce_kernel<!kMx, C, B, N>), rg, rb, 0, s, b.part, used, a.T, a.I, \
+                     a.Iq, a.Ik, a.d, a.a_scales, a.s_stride, a.chan_scale, a.bias, a.out, ssq)
+    switch (variant) {
+      case 0: QKVMX_SPLIT_REDUCE(false, false, false); break;
+      case 1: QKVMX_SPLIT_REDUCE(false, false, true); break;
+      case 2: QKVMX_SPLIT_REDUCE(false, true, false); break;
+      case 3: QKVMX_SPLIT_REDUCE(false, true, true); break;
+      case 4: QKVMX_SPLIT_REDUCE(true, false, false); break;
+      case 5: QKVMX_SPLIT_REDUCE(true, false, true); break;
+      case 6: QKVMX_SPLIT_REDUCE(true, true, false); break;
+      default: QKVMX_SPLIT_REDUCE(true, true, true); break;
+    }
+#undef QKVMX_SPLIT_REDUCE
+    e = hipGetLastError();
+  }
+  *err = e;
+  return true;
+}
+
 // Persistent project_kernel launch (one block per compute unit, each walking its XCD's tile
-// range), then the fixed-order sum of the partials when ssq is requested.
+// range), then the fixed-order sum of the partials when ssq is requested.  Calls with few
+// tiles take the split contraction instead when `planes` is given.
 template <bool kMx>
 hipError_t launch_core(const ProjectArgs& a, bool chan, bool bias, bool nbsd, float* ssq,
-                       hipStream_t s) {
+                       hipStream_t s, uint8_t* planes) {
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
+  if (launch_split<kMx>(a, chan, bias, nbsd, ssq, planes, cus, s, &e)) return e;
   const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n;
   const unsigned nblocks = (unsigned)std::min<int64_t>(ntiles, std::max(cus, 1));
   const dim3 grid(nblocks), block(kThreads);

@@ -28,7 +28,8 @@ hipError_t launch_project_mx(const uint8_t* a_codes, int64_t a_stride, const uin
                      reinterpret_cast<uint32_t*>(ws + mx_scale_image_offset(T, H)));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_core<true>(a, chan_scale, bias, nbsd, ssq, s);
+  return launch_core<true>(a, chan_scale, bias, nbsd, ssq, s,
+                           ws + mx_counters_offset(T, H, I) + kCounterBytes);
 }
 
 hipError_t launch_project_mx_staged(const uint8_t* img, const uint32_t* eimg,
@@ -44,7 +45,8 @@ hipError_t launch_project_mx_staged(const uint8_t* img, const uint32_t* eimg,
   hipLaunchKernelGGL(reset_counters_kernel, dim3(1), dim3(64), 0, s, a.ctr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_core<true>(a, chan_scale, bias, nbsd, ssq, s);
+  return launch_core<true>(a, chan_scale, bias, nbsd, ssq, s,
+                           ws + staged_counters_offset(T, I) + kCounterBytes);
 }
 
 }  // namespace qkvmx

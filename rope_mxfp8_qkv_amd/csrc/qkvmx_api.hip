@@ -281,6 +281,12 @@ size_t qkv_staged_workspace_bytes(int64_t T, int64_t I) {
   return staged_workspace_total_bytes(T, I);
 }
 
+int32_t qkvmx_projection_k_chunks(int64_t T, int64_t H, int64_t I, int32_t layout) {
+  if (T <= 0 || H <= 0 || H % 32 || I <= 0 || I % 16) return 0;
+  if (layout != QKVMX_LAYOUT_BSD && layout != QKVMX_LAYOUT_NBSD) return 0;
+  return split_plan(T, H, I).chunks;
+}
+
 qkvmx_status qkv_rowmx_project_staged(const uint8_t* act_image, size_t image_bytes,
                                       const float* row_scale, const void* w_packed,
                                       const float* w_channel_scale, const uint16_t* bias,

@@ -58,6 +58,29 @@ def test_size_queries():
     assert L.qkv_act_image_bytes(300, 2080) == 2 * 36 * 16384
     assert L.qkv_act_image_bytes(4, 100) == 0
     assert L.qkv_staged_workspace_bytes(75600, 15360) == 120 * 75600 * 8 + 256
+    # few tiles: + min(3, 256 // tiles) fp32 [T, I] planes of the split contraction
+    # (512 x 5120: 2 x 20 = 40 tiles -> 3 planes; partials 40 x 512 x 8 bytes)
+    assert L.qkv_staged_workspace_bytes(512, 5120) == 40 * 512 * 8 + 256 + 3 * 512 * 5120 * 4
+    assert (L.qkvmx_workspace_bytes(512, 5120, 5120)
+            == 2 * 80 * 16384 + 40 * 512 * 8 + 256 + 3 * 512 * 5120 * 4)
+
+
+def test_split_contraction_plan():
+    """K chunks per call: supersteps of 256 K-bytes cut into min(3, 256 // tiles) chunks of
+    ceil(supersteps / that) supersteps, at most 128 tiles, either output layout."""
+    L = _lib()
+    f = L.qkvmx_projection_k_chunks
+    assert f(512, 5120, 5120, 0) == 3          # 40 tiles -> 3-way, 20 supersteps -> 7, 7, 6
+    assert f(512, 5120, 5120, 1) == 3          # NBSd: the same plan
+    assert f(512, 1792, 5120, 0) == 3          # 7 supersteps -> 3, 3, 1
+    assert f(300, 512, 640, 0) == 2            # 6 tiles -> 3-way, but 2 supersteps
+    assert f(512, 512 * 3, 5120, 0) == 3       # 6 supersteps -> 2, 2, 2
+    assert f(128, 256, 384, 0) == 1            # one superstep
+    assert f(75600, 5120, 15360, 0) == 1       # 17760 tiles
+    assert f(4096, 5120, 15360, 0) == 1        # 960 tiles
+    assert f(1100, 512, 6528, 0) == 1          # 130 tiles
+    assert f(32768, 5120, 256, 0) == 2         # 128 tiles -> 2-way
+    assert f(0, 256, 384, 0) == 0 and f(4, 250, 384, 0) == 0 and f(4, 256, 384, 7) == 0
     assert L.qkv_staged_workspace_bytes(0, 16) == 0
 
 
