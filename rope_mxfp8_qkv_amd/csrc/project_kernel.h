@@ -760,8 +760,9 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   // quads (4 consecutive channels of one token, 16 bytes) through a buffer descriptor over
   // the unit's [T, I] plane.  Quads outside [T, I] get an offset beyond the descriptor's range
   // and the hardware drops them, so all 64 stores are issued unconditionally and the next
-  // unit's wait for all but the last kTailStores memory operations covers its DMAs.  The host
-  // keeps T * I * 4 < 2^31 for split calls.
+  // unit's wait for all but the last kTailStores memory operations covers its DMAs.  Split
+  // calls have at most 128 tiles of 256 x 256, so a plane holds at most 2^25 bytes and every
+  // offset fits the descriptor's 32 bits.
   auto split_store = [&](Tile u, bool more) __attribute__((always_inline)) {
     if (more) {
       issue(I0{}, 0);
