@@ -269,7 +269,7 @@ def run_gpu(args):
     if mx and args.act_layout == "packed":
         codes_a = torch.empty((T, H), dtype=torch.uint8, device=dev)
         e8_a = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
-    staged = not hn and args.act_layout == "staged"
+    staged = args.act_layout == "staged"
     if staged:
         img = torch.empty(q.qkv_act_image_bytes(T, H), dtype=torch.uint8, device=dev)
         if mx:
@@ -316,11 +316,14 @@ def run_gpu(args):
         if ev:
             ev[1].record(stream)
         if hn:
-            q.qkv_rowmx_project_headnorm(packed, wp, out, H=H, num_heads=p.num_heads,
-                                         num_kv_heads=p.num_kv_heads, head_dim=p.head_dim,
-                                         norm_kind=hn, q_gamma=hgq, k_gamma=hgk, q_beta=hbq,
-                                         k_beta=hbk, eps=1e-6, cos=inp["cos"], sin=inp["sin"],
-                                         bias=inp["bias"], workspace=ws, layout=layout)
+            hkw = dict(H=H, num_heads=p.num_heads, num_kv_heads=p.num_kv_heads,
+                       head_dim=p.head_dim, norm_kind=hn, q_gamma=hgq, k_gamma=hgk, q_beta=hbq,
+                       k_beta=hbk, eps=1e-6, cos=inp["cos"], sin=inp["sin"], bias=inp["bias"],
+                       workspace=ws, layout=layout)
+            if staged:
+                q.qkv_rowmx_project_headnorm_staged(img, row_scale, wp, out, **hkw)
+            else:
+                q.qkv_rowmx_project_headnorm(packed, wp, out, **hkw)
         elif mx and staged:
             q.qkv_mx_project_staged(img, eimg, wp, out, T=T, H=H, num_heads=p.num_heads,
                                     num_kv_heads=p.num_kv_heads, head_dim=p.head_dim,
@@ -715,7 +718,9 @@ def main():
                        if r["mx"] and r["staged"] else
                        "qkv_mx_project (activation repacks + project_kernel + ssq_reduce)"
                        if r["mx"] else
-                       "qkv_rowmx_project_headnorm (activation repack + project_kernel)"
+                       ("qkv_rowmx_project_headnorm_staged (counter reset + project_kernel)"
+                        if r["staged"] else
+                        "qkv_rowmx_project_headnorm (activation repack + project_kernel)")
                        if r["headnorm"] != "none" else
                        "qkv_rowmx_project_staged (counter reset + project_kernel + ssq_reduce)"
                        if r["staged"] else

@@ -305,6 +305,25 @@ qkvmx_status qkv_rowmx_project_headnorm(const uint8_t* a_codes, int64_t a_row_st
                                          uint16_t* out, void* workspace, size_t ws_bytes,
                                          hipStream_t stream);
 
+/* qkv_rowmx_project_headnorm on staged activations (act_image, row_scale written by
+ * row_quantize_staged or rmsnorm_mx_quantize_staged for the same T and H): the same out, bit for
+ * bit, as qkv_rowmx_project_headnorm on the packed rows of the same codes and scales, without
+ * the per-call activation re-layout.
+ *   image_bytes  >= qkv_act_image_bytes(T, H); act_image 256-byte aligned.
+ *   workspace    >= qkv_staged_workspace_bytes(T, I) bytes, 256-byte aligned, required; scratch.
+ * Other arguments, layouts, requirements and errors as qkv_rowmx_project_headnorm. */
+qkvmx_status qkv_rowmx_project_headnorm_staged(const uint8_t* act_image, size_t image_bytes,
+                                                const float* row_scale, const void* w_packed,
+                                                const uint16_t* bias, int64_t T, int64_t H,
+                                                int32_t num_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t layout,
+                                                int32_t norm_kind, const uint16_t* q_gamma,
+                                                const uint16_t* k_gamma, const uint16_t* q_beta,
+                                                const uint16_t* k_beta, float eps,
+                                                const float* cos_tab, const float* sin_tab,
+                                                uint16_t* out, void* workspace, size_t ws_bytes,
+                                                hipStream_t stream);
+
 /* Workspace bytes qkv_mx_project needs for a [T, H] x [H, I] call: the activation codes and
  * their exponents re-laid in the kernel's LDS stage images (about T * H * 33 / 32 bytes) plus
  * per-tile sums of squares and, for calls with few tiles, the split contraction's planes (as

@@ -25,7 +25,7 @@ __all__ = [
     "HEAD_LAYER_NORM", "qkv_act_image_bytes", "row_quantize_staged", "rmsnorm_mx_quantize_staged",
     "qkv_staged_workspace_bytes", "qkv_rowmx_project_staged", "mfma_rate_probe",
     "qkv_act_exp_image_bytes", "mx_block_quantize_staged", "rmsnorm_mx_block_quantize_staged",
-    "qkv_mx_project_staged", "projection_k_chunks",
+    "qkv_mx_project_staged", "projection_k_chunks", "qkv_rowmx_project_headnorm_staged",
 ]
 
 
@@ -288,6 +288,23 @@ def qkv_rowmx_project_headnorm(packed_a, w_packed, out, *, H: int, num_heads: in
                                             _ptr(k_beta), float(eps), _ptr(cos), _ptr(sin),
                                             _ptr(out), ws_ptr, ws_n, _stream(stream)),
            "qkv_rowmx_project_headnorm")
+
+
+def qkv_rowmx_project_headnorm_staged(act_image, row_scale, w_packed, out, *, H: int,
+                                      num_heads: int, num_kv_heads: int, head_dim: int,
+                                      norm_kind: int, q_gamma, k_gamma=None, q_beta=None,
+                                      k_beta=None, eps: float = 1e-6, cos=None, sin=None,
+                                      bias=None, workspace=None, layout: int = LAYOUT_BSD,
+                                      stream=None):
+    """qkv_rowmx_project_headnorm on staged ROW_MX activations (``act_image`` from a staged
+    producer, fp32 ``row_scale`` [T]); T is taken from ``row_scale``."""
+    T = row_scale.shape[0]
+    ws_ptr, ws_n = (None, 0) if workspace is None else (_ptr(workspace), _nbytes(workspace))
+    _check(lib().qkv_rowmx_project_headnorm_staged(
+        _ptr(act_image), _nbytes(act_image), _ptr(row_scale), _ptr(w_packed), _ptr(bias), T, H,
+        num_heads, num_kv_heads, head_dim, layout, norm_kind, _ptr(q_gamma), _ptr(k_gamma),
+        _ptr(q_beta), _ptr(k_beta), float(eps), _ptr(cos), _ptr(sin), _ptr(out), ws_ptr, ws_n,
+        _stream(stream)), "qkv_rowmx_project_headnorm_staged")
 
 
 def qk_norm_rope_apply(qkv, *, num_heads: int, num_kv_heads: int, head_dim: int, eps: float,

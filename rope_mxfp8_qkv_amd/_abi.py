@@ -45,6 +45,10 @@ SIGNATURES = {
     "qkv_rowmx_project_headnorm": (c_i32, [c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_i64, c_i32,
                                            c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_f,
                                            c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "qkv_rowmx_project_headnorm_staged": (c_i32, [c_vp, c_sz, c_vp, c_vp, c_vp, c_i64, c_i64,
+                                                  c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp,
+                                                  c_vp, c_vp, c_f, c_vp, c_vp, c_vp, c_vp, c_sz,
+                                                  c_vp]),
     "qkv_mx_project": (c_i32, [c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_i64, c_i64, c_i32,
                                c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "qkv_act_image_bytes": (c_sz, [c_i64, c_i64]),

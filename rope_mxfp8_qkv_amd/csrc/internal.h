@@ -180,6 +180,14 @@ hipError_t launch_project_headnorm(const uint8_t* a_codes, int64_t a_stride,
                                    const uint16_t* k_beta, float eps, const float* cos_tab,
                                    const float* sin_tab, uint16_t* out, uint8_t* ws,
                                    hipStream_t s);
+hipError_t launch_project_headnorm_staged(const uint8_t* img, const float* row_scale,
+                                          const uint8_t* w_packed, const uint16_t* bias,
+                                          int64_t T, int64_t H, int64_t I, int64_t Iq,
+                                          int64_t Ik, int64_t d, bool nbsd, int norm_kind,
+                                          const uint16_t* q_gamma, const uint16_t* k_gamma,
+                                          const uint16_t* q_beta, const uint16_t* k_beta,
+                                          float eps, const float* cos_tab, const float* sin_tab,
+                                          uint16_t* out, uint8_t* ws, hipStream_t s);
 hipError_t launch_mx_quantize(const void* x, int dtype, int64_t T, int64_t H, uint8_t* codes,
                               uint8_t* e8, hipStream_t s);
 hipError_t launch_rmsnorm_mx(const uint16_t* hid, const uint16_t* res, const uint16_t* gamma,

@@ -322,19 +322,14 @@ qkvmx_status qkv_rowmx_project_staged(const uint8_t* act_image, size_t image_byt
                                           (uint8_t*)workspace, stream), fn);
 }
 
-qkvmx_status qkv_rowmx_project_headnorm(const uint8_t* a_codes, int64_t a_row_stride,
-                                         const uint8_t* a_scales, int64_t a_scale_stride,
-                                         const void* w_packed, const uint16_t* bias, int64_t T,
-                                         int64_t H, int32_t num_heads, int32_t num_kv_heads,
-                                         int32_t head_dim, int32_t layout, int32_t norm_kind,
-                                         const uint16_t* q_gamma, const uint16_t* k_gamma,
-                                         const uint16_t* q_beta, const uint16_t* k_beta,
-                                         float eps, const float* cos_tab, const float* sin_tab,
-                                         uint16_t* out, void* workspace, size_t ws_bytes,
-                                         hipStream_t stream) {
-  const char* fn = "qkv_rowmx_project_headnorm";
-  if (!a_codes || !a_scales || !w_packed || !out) return fail(QKVMX_ERR_NULL, "%s: null pointer", fn);
-  if (!workspace) return fail(QKVMX_ERR_WORKSPACE, "%s: workspace is required", fn);
+// Checks shared by the two per-head qk-norm projections (norm kind, shapes, the head geometry
+// the fused epilogue supports, layout, gamma / beta / table pairing, eps); QKVMX_OK if they hold.
+static qkvmx_status check_headnorm(const char* fn, int64_t T, int64_t H, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t layout,
+                                   int32_t norm_kind, const uint16_t* q_gamma,
+                                   const uint16_t* k_gamma, const uint16_t* q_beta,
+                                   const uint16_t* k_beta, float eps, const float* cos_tab,
+                                   const float* sin_tab) {
   if (norm_kind != QKVMX_HEAD_RMS_NORM && norm_kind != QKVMX_HEAD_LAYER_NORM)
     return fail(QKVMX_ERR_ARG, "%s: norm_kind must be QKVMX_HEAD_RMS_NORM or QKVMX_HEAD_LAYER_NORM", fn);
   if (T <= 0 || H <= 0 || H % 32) return fail(QKVMX_ERR_SHAPE, "%s: need T > 0, H %% 32 == 0", fn);
@@ -352,6 +347,26 @@ qkvmx_status qkv_rowmx_project_headnorm(const uint8_t* a_codes, int64_t a_row_st
   if (k_beta && num_kv_heads == 0) return fail(QKVMX_ERR_ARG, "%s: k_beta without a K segment", fn);
   if ((cos_tab == nullptr) != (sin_tab == nullptr)) return fail(QKVMX_ERR_ARG, "%s: cos_tab and sin_tab come together", fn);
   if (!(eps >= 0.0f)) return fail(QKVMX_ERR_ARG, "%s: eps must be >= 0", fn);
+  return QKVMX_OK;
+}
+
+qkvmx_status qkv_rowmx_project_headnorm(const uint8_t* a_codes, int64_t a_row_stride,
+                                         const uint8_t* a_scales, int64_t a_scale_stride,
+                                         const void* w_packed, const uint16_t* bias, int64_t T,
+                                         int64_t H, int32_t num_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t layout, int32_t norm_kind,
+                                         const uint16_t* q_gamma, const uint16_t* k_gamma,
+                                         const uint16_t* q_beta, const uint16_t* k_beta,
+                                         float eps, const float* cos_tab, const float* sin_tab,
+                                         uint16_t* out, void* workspace, size_t ws_bytes,
+                                         hipStream_t stream) {
+  const char* fn = "qkv_rowmx_project_headnorm";
+  if (!a_codes || !a_scales || !w_packed || !out) return fail(QKVMX_ERR_NULL, "%s: null pointer", fn);
+  if (!workspace) return fail(QKVMX_ERR_WORKSPACE, "%s: workspace is required", fn);
+  const qkvmx_status hs = check_headnorm(fn, T, H, num_heads, num_kv_heads, head_dim, layout,
+                                         norm_kind, q_gamma, k_gamma, q_beta, k_beta, eps,
+                                         cos_tab, sin_tab);
+  if (hs != QKVMX_OK) return hs;
   if (a_row_stride < H || a_row_stride % 4 || a_scale_stride <= 0 || a_scale_stride % 4)
     return fail(QKVMX_ERR_SHAPE, "%s: a_row_stride >= H and strides multiples of 4", fn);
   const int64_t I = (int64_t)(num_heads + 2 * (int64_t)num_kv_heads) * head_dim;
@@ -372,6 +387,46 @@ qkvmx_status qkv_rowmx_project_headnorm(const uint8_t* a_codes, int64_t a_row_st
                                             head_dim, layout == QKVMX_LAYOUT_NBSD, norm_kind,
                                             q_gamma, k_gamma, q_beta, k_beta, eps, cos_tab,
                                             sin_tab, out, (uint8_t*)workspace, stream), fn);
+}
+
+qkvmx_status qkv_rowmx_project_headnorm_staged(const uint8_t* act_image, size_t image_bytes,
+                                                const float* row_scale, const void* w_packed,
+                                                const uint16_t* bias, int64_t T, int64_t H,
+                                                int32_t num_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t layout,
+                                                int32_t norm_kind, const uint16_t* q_gamma,
+                                                const uint16_t* k_gamma, const uint16_t* q_beta,
+                                                const uint16_t* k_beta, float eps,
+                                                const float* cos_tab, const float* sin_tab,
+                                                uint16_t* out, void* workspace, size_t ws_bytes,
+                                                hipStream_t stream) {
+  const char* fn = "qkv_rowmx_project_headnorm_staged";
+  if (!act_image || !row_scale || !w_packed || !out) return fail(QKVMX_ERR_NULL, "%s: null pointer", fn);
+  if (!workspace) return fail(QKVMX_ERR_WORKSPACE, "%s: workspace is required", fn);
+  const qkvmx_status hs = check_headnorm(fn, T, H, num_heads, num_kv_heads, head_dim, layout,
+                                         norm_kind, q_gamma, k_gamma, q_beta, k_beta, eps,
+                                         cos_tab, sin_tab);
+  if (hs != QKVMX_OK) return hs;
+  if (image_bytes < act_image_bytes(T, H))
+    return fail(QKVMX_ERR_SHAPE, "%s: image_bytes %zu < %zu", fn, image_bytes, act_image_bytes(T, H));
+  const int64_t I = (int64_t)(num_heads + 2 * (int64_t)num_kv_heads) * head_dim;
+  if (I * 2 * 256 >= kMaxOffset) return fail(QKVMX_ERR_UNSUPPORTED, "%s: I must be < 2^22", fn);
+  if (layout == QKVMX_LAYOUT_NBSD && 2 * ((256 + (int64_t)head_dim) * T + 257 * (int64_t)head_dim) >= kMaxOffset)
+    return fail(QKVMX_ERR_UNSUPPORTED, "%s: NBSd needs 2 ((256 + head_dim) T + 257 head_dim) < 2^31", fn);
+  if (ws_bytes < staged_workspace_total_bytes(T, I))
+    return fail(QKVMX_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, staged_workspace_total_bytes(T, I));
+  if (!aligned(act_image, 256) || !aligned(row_scale, 4) || !aligned(w_packed, 256) ||
+      (bias && !aligned(bias, 8)) || !aligned(out, 16) || !aligned(workspace, 256) ||
+      !aligned(q_gamma, 8) || (k_gamma && !aligned(k_gamma, 8)) || (q_beta && !aligned(q_beta, 8)) ||
+      (k_beta && !aligned(k_beta, 8)) || (cos_tab && !aligned(cos_tab, 16)) || (sin_tab && !aligned(sin_tab, 16)))
+    return fail(QKVMX_ERR_ALIGN, "%s: alignment (act_image/w_packed/workspace 256, row_scale 4, bias/gamma/beta 8, out/tables 16)", fn);
+  const int64_t Iq = (int64_t)num_heads * head_dim, Ik = (int64_t)num_kv_heads * head_dim;
+  return hip_status(launch_project_headnorm_staged(act_image, row_scale, (const uint8_t*)w_packed,
+                                                   bias, T, H, I, Iq, Ik, head_dim,
+                                                   layout == QKVMX_LAYOUT_NBSD, norm_kind,
+                                                   q_gamma, k_gamma, q_beta, k_beta, eps,
+                                                   cos_tab, sin_tab, out, (uint8_t*)workspace,
+                                                   stream), fn);
 }
 
 size_t qkv_mx_workspace_bytes(int64_t T, int64_t H, int64_t I) {

@@ -279,3 +279,50 @@ def test_mx_path_validation():
     assert L.rmsnorm_mx_block_quantize(P, None, P, 1e-6, 4, 256, 0, None, P, P, P + 8, None) == 3
     assert L.rmsnorm_mx_block_quantize(P, None, P, -1.0, 4, 256, 0, None, P, P, None, None) == 4
     assert L.rmsnorm_mx_block_quantize(None, None, P, 1e-6, 4, 256, 0, None, P, P, None, None) == 1
+
+
+def _hnproj(L, staged, **kw):
+    if staged:
+        a = dict(act_image=P, image_bytes=1 << 30, row_scale=P, w_packed=P, bias=None, T=4,
+                 H=256, num_heads=2, num_kv_heads=2, head_dim=64, layout=0, norm_kind=1,
+                 q_gamma=P, k_gamma=P, q_beta=None, k_beta=None, eps=1e-6, cos_tab=None,
+                 sin_tab=None, out=P, workspace=P, ws_bytes=1 << 30, stream=None)
+        a.update(kw)
+        return L.qkv_rowmx_project_headnorm_staged(*a.values())
+    a = dict(a_codes=P, a_row_stride=260, a_scales=P + 256, a_scale_stride=260, w_packed=P,
+             bias=None, T=4, H=256, num_heads=2, num_kv_heads=2, head_dim=64, layout=0,
+             norm_kind=1, q_gamma=P, k_gamma=P, q_beta=None, k_beta=None, eps=1e-6, cos_tab=None,
+             sin_tab=None, out=P, workspace=P, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return L.qkv_rowmx_project_headnorm(*a.values())
+
+
+@pytest.mark.parametrize("staged", [False, True], ids=["packed", "staged"])
+def test_headnorm_validation(staged):
+    """The per-head qk-norm projections (rows and staged) reject every invalid argument on the
+    host with the documented status."""
+    L = _lib()
+    f = lambda **kw: _hnproj(L, staged, **kw)
+    assert f(w_packed=None) == 1
+    assert f(out=None) == 1
+    assert f(**({"act_image": None} if staged else {"a_codes": None})) == 1
+    assert f(workspace=None) == 5
+    assert f(norm_kind=0) == 4 and f(norm_kind=3) == 4
+    assert f(T=0) == 2 and f(H=100) == 2
+    assert f(head_dim=96) == 6                          # fused epilogue: d = 64 or 128
+    assert f(num_heads=1) == 6                          # Q segment of 64 channels
+    assert f(layout=2) == 4
+    assert f(q_gamma=None) == 4 and f(k_gamma=None) == 4
+    assert f(num_kv_heads=0) == 4                       # k_gamma given without a K segment
+    assert f(q_beta=P) == 4                             # beta with RMS_NORM
+    assert f(norm_kind=2, q_beta=P, k_beta=P, ws_bytes=100) == 5   # LAYER_NORM takes betas
+    assert f(cos_tab=P) == 4                            # cos without sin
+    assert f(eps=-1.0) == 4 and f(eps=float("nan")) == 4
+    assert f(ws_bytes=100) == 5
+    assert f(q_gamma=P + 2) == 3 and f(out=P + 8) == 3
+    if staged:
+        assert f(image_bytes=100) == 2
+        assert f(act_image=P + 16) == 3
+        assert f(row_scale=P + 2) == 3
+    else:
+        assert f(a_row_stride=100) == 2

@@ -2,7 +2,8 @@
 rotate-half RoPE fused into its epilogue ([QKV-CTE] "Upstream behavior"), against the oracle's
 pass 1 followed by its per-head norm and RoPE (fp64, one bf16 rounding on the GPU side only).
 Covers head_dim 64 and 128, LayerNorm with and without beta, RoPE on and off, GQA, a single
-segment, ragged T and I, T = 1 and both output layouts; and the unsupported shapes."""
+segment, ragged T and I, T = 1 and both output layouts, with the staged hand-over giving the
+same bytes as the packed rows; and the unsupported shapes."""
 import numpy as np
 import pytest
 
@@ -50,19 +51,26 @@ def test_headnorm_parity(name, p, kind, rope, beta, layout):
     out = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(q.qkvmx_workspace_bytes(p.T, p.H, p.I), dtype=torch.uint8, device=dev)
     opt = lambda a: None if a is None else G.bf16_dev(a, dev)
-    q.qkv_rowmx_project_headnorm(G.to_dev(inp.packed, dev), wp, out, H=p.H,
-                                 num_heads=p.num_heads, num_kv_heads=p.num_kv_heads, head_dim=d,
-                                 norm_kind=kind, q_gamma=opt(gq), k_gamma=opt(gk),
-                                 q_beta=opt(bq), k_beta=opt(bk), eps=1e-6,
-                                 cos=None if cos is None else G.to_dev(cos, dev),
-                                 sin=None if sin is None else G.to_dev(sin, dev),
-                                 bias=G.bf16_dev(inp.bias, dev), workspace=ws,
-                                 layout=q.LAYOUT_NBSD if layout == "nbsd" else q.LAYOUT_BSD)
+    kw = dict(H=p.H, num_heads=p.num_heads, num_kv_heads=p.num_kv_heads, head_dim=d,
+              norm_kind=kind, q_gamma=opt(gq), k_gamma=opt(gk), q_beta=opt(bq), k_beta=opt(bk),
+              eps=1e-6, cos=None if cos is None else G.to_dev(cos, dev),
+              sin=None if sin is None else G.to_dev(sin, dev), bias=G.bf16_dev(inp.bias, dev),
+              layout=q.LAYOUT_NBSD if layout == "nbsd" else q.LAYOUT_BSD)
+    q.qkv_rowmx_project_headnorm(G.to_dev(inp.packed, dev), wp, out, workspace=ws, **kw)
+    # the staged hand-over of the same codes and scales (the staged encoder matches the oracle's
+    # rows bit for bit): the same bytes, without the per-call re-layout
+    img = torch.empty(q.qkv_act_image_bytes(p.T, p.H), dtype=torch.uint8, device=dev)
+    sc = torch.empty((p.T,), dtype=torch.float32, device=dev)
+    q.row_quantize_staged(G.to_dev(inp.x, dev), img, sc)
+    out_s = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    ws_s = torch.empty(q.qkv_staged_workspace_bytes(p.T, p.I), dtype=torch.uint8, device=dev)
+    q.qkv_rowmx_project_headnorm_staged(img, sc, wp, out_s, workspace=ws_s, **kw)
     torch.cuda.synchronize()
     got = G.bf16_host(out)
     if layout == "nbsd":
         got = oracle.nbsd_to_bsd(got)
     G.check_close(got, ref, f"{name} output")
+    assert torch.equal(out_s.view(torch.int16), out.view(torch.int16)), f"{name}: staged != rows"
 
 
 def test_headnorm_unsupported_shapes():
