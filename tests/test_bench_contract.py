@@ -1,0 +1,54 @@
+"""Host-side parts of bench.py (no GPU): the one-GPU guard, the algorithmic byte counts the
+roofline and stage rates divide by, and the traffic record's bookkeeping."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import synth  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in line["error"]
+
+
+def test_algorithmic_bytes_at_the_video_shape():
+    """Pass 2: bf16 Q/K read + write, fp32 cos and sin rows, the two sums per token and the two
+    gammas; producer: hidden + residual read, residual sum written, ROW_MX rows (H codes + fp32
+    scale) or MX rows (H codes + H / 32 exponents) written, gamma read."""
+    p = synth.CONFIGS[5].calls[0]
+    T, H, Iq, Ik, d = p.T, p.H, p.Iq, p.Ik, p.head_dim
+    assert (T, H, Iq, Ik, d) == (75600, 5120, 5120, 5120, 128)
+    b = bench.algorithmic_bytes(p, producer=True)
+    assert b["norm_rope"] == 4 * T * (Iq + Ik) + 8 * T * d + 8 * T + 2 * (Iq + Ik)
+    assert b["norm_rope"] == pytest.approx(3.175e9, rel=2e-4)      # 3.175 GB per step
+    assert b["producer"] == 6 * T * H + T * (H + 4) + 2 * H
+    assert b["producer"] == pytest.approx(2.710e9, rel=2e-4)       # 2.710 GB per step
+    bm = bench.algorithmic_bytes(p, producer=True, mx=True)
+    assert bm["producer"] == 6 * T * H + T * (H + H // 32) + 2 * H
+    assert bench.algorithmic_bytes(p, producer=False)["producer"] == 0
+
+
+def test_traffic_record_is_tied_to_the_projection_sources():
+    """The committed record names the sources it was measured on; a record with another digest
+    is never reported."""
+    with open(bench.TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    assert set(rec["per_kernel"]) >= {"project_kernel", "ssq_reduce_kernel"}
+    assert rec["hbm_bytes_per_call"] == pytest.approx(
+        sum(v["read_bytes"] + v["write_bytes"] for v in rec["per_kernel"].values()))
+    digest = bench.source_digest(bench.PROJECT_SRC)
+    assert len(digest) == 16
+    if rec["kernel_src_sha256_16"] == digest:
+        assert bench.measured_traffic(bench.STAGED_KERNELS) == pytest.approx(
+            rec["hbm_bytes_per_call"])
