@@ -662,8 +662,9 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
-                                   "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        print(json.dumps({"error": "the benchmark runs on exactly one GPU; --gpus must be 1 "
+                                   "(the path shards by tokens with no exchange; multi-GPU runs "
+                                   "are not part of this benchmark)"}))
         sys.exit(2)
     if synth_configs_separate(args.config):
         run_gpu_separate(args)

@@ -7,7 +7,8 @@ I = (num_q_heads + 2 * num_kv_heads) * d_head and the output columns ordered Q |
 then dequantised, bias-added and stored.  "Interface": ``weight_scales`` is a per-output-channel
 fp32 dequant scale ``[1, I]``; ``bias`` is ``[1, I]``; the result is bf16.
 
-Dequantisation used (the plain reading of the two scale kinds):
+Dequantisation used (the plain reading of the two scale kinds: the pages' per-channel fp32
+weight scale and the MX weight's per-32 E8M0 exponents both apply, and multiply):
   X[s, i] = sA[s] * c[i] * sum_h dec(A[s, h]) * dec(W[h, i]) * 2^(E[h // 32, i] - 127) + bias[i]
 with sA the row's fp32 ROW_MX scale, c the per-channel weight scale (1 when absent) and E the
 block exponent.  With MX block-32 activations ([RMSNORM-MX] ``qmx_output_dtype``) the row scale
