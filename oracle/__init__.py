@@ -20,7 +20,7 @@ from .codecs import (e4m3_decode, e4m3_encode, e8m0_decode, bf16_round_f32, bf16
                      f64_to_bf16)
 from .rowmx import rowmx_quantize, rowmx_unpack
 from .mxweight import mx_weight_quantize, mx_weight_decode
-from .gemm import project, segment_ssq
+from .gemm import project, segment_ssq, abs_term_sum
 from .norm_rope import inv_rms, norm_rope
 from .producer import rmsnorm_rowmx, rmsnorm_mx
 from .mxact import mx_block_quantize, mx_block_decode
@@ -30,6 +30,6 @@ from .headnorm import head_norm_rope, RMS_NORM, LAYER_NORM
 __all__ = [
     "e4m3_decode", "e4m3_encode", "e8m0_decode", "bf16_round_f32", "bf16_to_f64", "f64_to_bf16",
     "rowmx_quantize", "rowmx_unpack", "mx_weight_quantize", "mx_weight_decode",
-    "project", "segment_ssq", "inv_rms", "norm_rope", "rmsnorm_rowmx", "rmsnorm_mx", "mx_block_quantize", "mx_block_decode", "bsd_to_nbsd", "nbsd_to_bsd",
+    "project", "segment_ssq", "abs_term_sum", "inv_rms", "norm_rope", "rmsnorm_rowmx", "rmsnorm_mx", "mx_block_quantize", "mx_block_decode", "bsd_to_nbsd", "nbsd_to_bsd",
     "head_norm_rope", "RMS_NORM", "LAYER_NORM",
 ]

@@ -72,3 +72,24 @@ def project(a_codes, a_scale, w_codes, w_e8m0, w_channel_scale=None, bias_bf16=N
     if bias_bf16 is not None:
         X = X + bf16_to_f64(bias_bf16)[None, :]
     return X, segment_ssq(X, num_heads, num_kv_heads, head_dim)
+
+
+def abs_term_sum(a_codes, a_scale, w_codes, w_e8m0, w_channel_scale=None, *, a_e8m0=None):
+    """Per output, the sum of the absolute values of the contraction's terms, float64 [T, I]:
+    |sA[s] * c[i]| * sum_h |dec(A[s, h]) * dec(W[h, i]) * 2^(E[h // 32, i] - 127)| (with MX
+    activations the per-block factor inside the sum, as in ``project``).
+
+    This is the scale against which a summation error is measured: any summation of the terms
+    whose every addition is exact to a relative error e lies within about (depth) * e times this
+    value of the exact sum; an accumulator that rounds each partial sum relative to its inputs'
+    magnitudes is bounded by a multiple of it even where the terms cancel."""
+    if a_e8m0 is not None:
+        A = np.abs(mx_block_decode(a_codes, a_e8m0))
+        sA = np.ones(A.shape[0])
+    else:
+        A = np.abs(e4m3_decode(a_codes))
+        sA = np.abs(np.asarray(a_scale, dtype=np.float32).astype(np.float64))
+    W = np.abs(mx_weight_decode(w_codes, w_e8m0))
+    c = (np.ones(W.shape[1]) if w_channel_scale is None
+         else np.abs(np.asarray(w_channel_scale, dtype=np.float32).astype(np.float64)))
+    return (A @ W) * sA[:, None] * c[None, :]

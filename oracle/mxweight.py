@@ -62,8 +62,9 @@ def _quantize_rows(w):
     # E = X + 127 clamped to the finite E8M0 range [0, 254]; the element scale is 2^(E - 127)
     E = np.where(nz, np.clip(fl - 8 + 127, 0, 254), 0)
     X = E - 127
-    # w / 2^X is exact in fp32 for these magnitudes (power-of-two scaling, no under/overflow
-    # for |w| >= 2^-100); computed in fp64 and narrowed exactly.
+    # w / 2^X is exact in fp32: X >= -127, so a finite fp32 w (subnormals included) scales to
+    # a value with at most 24 significant bits and magnitude between 2^-22 and 2^9; computed in
+    # fp64 and narrowed exactly (checked below).
     scaled = blocks.astype(np.float64) * np.ldexp(1.0, -X)[:, None, :]
     scaled32 = scaled.astype(np.float32)
     if not np.array_equal(scaled32.astype(np.float64), scaled):

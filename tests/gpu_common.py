@@ -101,6 +101,34 @@ def propagated_bound(X: np.ndarray, ssq: np.ndarray, gq, gk, nq, nkv, d, eps, no
     return out
 
 
+def floor_blocks(rng) -> list:
+    """32-element fp32 blocks that reach or straddle the lower clamp of the E8M0 exponent
+    (largest magnitude below 2^-119, fp32 subnormals, -0.0, exactly 2^-119 / 2^-120 / 2^-118)."""
+    f32 = np.float32
+    n = lambda s: (rng.standard_normal(32) * s).astype(f32)
+    blocks = [
+        n(1e-37),                                              # amax ~ 2^-122: E clamps to 0
+        n(1e-41),                                              # fp32 subnormals only
+        np.full(32, f32(2.0 ** -149)) * np.where(rng.random(32) < 0.5, 1, -1).astype(f32),
+        np.zeros(32, f32),                                     # all-zero block: E = 0, codes 0
+    ]
+    b = np.zeros(32, f32)                                      # one subnormal among zeros and -0
+    b[7] = f32(-3 * 2.0 ** -140)
+    b[8] = f32(-0.0)
+    blocks.append(b)
+    b = n(1e-39)                                               # subnormals with a normal max
+    b[3] = f32(2.0 ** -126)
+    blocks.append(b)
+    for e in (-119, -120, -118):                               # around the clamp boundary
+        b = (rng.uniform(-1, 1, 32) * 2.0 ** e).astype(f32)
+        b[0] = f32(2.0 ** e)                                   # amax exactly 2^e
+        blocks.append(b)
+    b = (rng.uniform(-1, 1, 32) * 2.0 ** -119).astype(f32)
+    b[5] = f32(np.nextafter(f32(2.0 ** -119), f32(0)))        # just below 2^-119
+    blocks.append(b)
+    return blocks
+
+
 @dataclasses.dataclass
 class ProjInputs:
     p: synth.Projection

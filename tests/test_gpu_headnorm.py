@@ -83,13 +83,19 @@ def test_headnorm_unsupported_shapes():
     out = torch.empty((4, 512), dtype=torch.bfloat16, device=dev)
     wp = torch.zeros(q.qkv_weight_packed_bytes(256, 512), dtype=torch.uint8, device=dev)
     packed = torch.zeros((4, 260), dtype=torch.uint8, device=dev)
+    g32 = torch.ones(32, dtype=torch.bfloat16, device=dev)
+    g64 = torch.ones(64, dtype=torch.bfloat16, device=dev)
+    out320 = torch.empty((4, 320), dtype=torch.bfloat16, device=dev)
+    wp320 = torch.zeros(q.qkv_weight_packed_bytes(256, 320), dtype=torch.uint8, device=dev)
     with pytest.raises(q.QkvmxError) as ei:           # head_dim 32
         q.qkv_rowmx_project_headnorm(packed, wp, out, H=256, num_heads=8, num_kv_heads=4,
-                                     head_dim=32, norm_kind=1, q_gamma=g, k_gamma=g, workspace=buf)
+                                     head_dim=32, norm_kind=1, q_gamma=g32, k_gamma=g32,
+                                     workspace=buf)
     assert ei.value.status == 6
     with pytest.raises(q.QkvmxError) as ei:           # Q segment of 192 channels
-        q.qkv_rowmx_project_headnorm(packed, wp, out, H=256, num_heads=3, num_kv_heads=1,
-                                     head_dim=64, norm_kind=1, q_gamma=g, k_gamma=g, workspace=buf)
+        q.qkv_rowmx_project_headnorm(packed, wp320, out320, H=256, num_heads=3, num_kv_heads=1,
+                                     head_dim=64, norm_kind=1, q_gamma=g64, k_gamma=g64,
+                                     workspace=buf)
     assert ei.value.status == 6
     with pytest.raises(q.QkvmxError) as ei:           # beta with RMS_NORM
         q.qkv_rowmx_project_headnorm(packed, wp, out, H=256, num_heads=2, num_kv_heads=1,

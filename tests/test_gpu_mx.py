@@ -52,6 +52,11 @@ def test_mx_block_quantize_bit_exact(dtype, H):
     x *= np.float32(50.0)
     x[5, :7] = -0.0                                   # signed zeros inside a non-zero block
     x[6, 40] = 1e6                                    # saturating element of its block
+    # blocks at the E8M0 floor (largest magnitude below 2^-119, fp32 subnormals, -0.0; in bf16
+    # the subnormal ones stay subnormal): exponent 0
+    fb = G.floor_blocks(np.random.default_rng(12))
+    for j, blk in enumerate(fb):
+        x[10 + j, 64:96] = blk
     if dtype == "bf16":
         bits = synth.to_bf16_bits(x)
         x = synth.bf16_bits_to_f32(bits)
@@ -59,6 +64,7 @@ def test_mx_block_quantize_bit_exact(dtype, H):
     else:
         xd = G.to_dev(x, dev)
     codes_ref, e8_ref = oracle.mx_block_quantize(x)
+    assert (e8_ref[10:10 + len(fb), 2] == 0).sum() >= 6   # the clamp is reached
     codes = torch.empty((T, H), dtype=torch.uint8, device=dev)
     e8 = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
     q.mx_block_quantize(xd, codes, e8)

@@ -34,8 +34,15 @@ def test_mx_weight_quantize_bit_exact(H, I):
     rng = np.random.default_rng(H + I)
     w = (0.02 * rng.standard_normal((H, I))).astype(np.float32)
     w[:32, 0] = 0.0                       # zero block
-    w[32:64, 1] *= 1e-30                  # tiny block (exponent clamps at the E8M0 floor)
+    w[32:64, 1] *= 1e-30                  # tiny block (amax ~ 2^-104: exponent 14)
     w[5, 2] = -3.0                        # saturating element
+    # blocks at the E8M0 floor (largest magnitude below 2^-119, fp32 subnormals, -0.0): the
+    # exponent clamps to 0; the oracle's exponents for them are pinned in rationals on the CPU
+    fb = G.floor_blocks(rng)
+    for j, blk in enumerate(fb):
+        w[64:96, 3 + j] = blk
+    ref_e8 = oracle.mx_weight_quantize(w)[1]
+    assert (ref_e8[2, 3:3 + len(fb)] == 0).sum() >= 6   # the clamp is reached
     codes_ref, e8_ref = oracle.mx_weight_quantize(w)
     codes = torch.empty((H // 4, I, 4), dtype=torch.uint8, device=dev)
     e8 = torch.empty((H // 32, I), dtype=torch.uint8, device=dev)

@@ -212,6 +212,9 @@ def test_mx_block_quantize_staged_bit_exact(dtype, H):
     dev = G.torch_dev()
     T = 300
     x = _blocky(T, H, 13)
+    fb = G.floor_blocks(np.random.default_rng(14))     # exponent clamps to 0 (E8M0 floor)
+    for j, blk in enumerate(fb):
+        x[20 + j, 96:128] = blk
     if dtype == "bf16":
         bits = synth.to_bf16_bits(x)
         x = synth.bf16_bits_to_f32(bits)
@@ -219,6 +222,7 @@ def test_mx_block_quantize_staged_bit_exact(dtype, H):
     else:
         xd = G.to_dev(x, dev)
     codes_ref, e8_ref = oracle.mx_block_quantize(x)
+    assert (e8_ref[20:20 + len(fb), 3] == 0).sum() >= 6
     img, eimg = _image(q, T, H, dev), _exp_image(q, T, H, dev)
     q.mx_block_quantize_staged(xd, img, eimg)
     torch.cuda.synchronize()

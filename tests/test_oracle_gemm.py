@@ -146,3 +146,46 @@ def test_ssq_excludes_v_and_handles_single_segment():
     assert np.allclose(ssq_q[:, 0], (Xq ** 2).sum(1), rtol=1e-14)
     with pytest.raises(ValueError):
         oracle.project(a, sa, w, e, num_heads=3, num_kv_heads=1, head_dim=d)
+
+
+def test_abs_term_sum_pins():
+    """abs_term_sum: exact rational brute force of sum_h |a_h w_h| 2^(E - 127) times |sA c| on a
+    tiny shape (with negative scales and MX activation exponents); equal to X - bias when every
+    code is non-negative; never below |X - bias| (triangle inequality)."""
+    rng = np.random.default_rng(70)
+    T, H, nq, nkv, d = 3, 64, 1, 1, 2
+    I = (nq + 2 * nkv) * d
+    a = _rand_codes(rng, (T, H))
+    wn = _rand_codes(rng, (H, I))
+    ew = rng.integers(118, 136, (H // 32, I)).astype(np.uint8)
+    w4 = _to_h4i4(wn)
+    sA = np.array([0.75, -2.0, 1e-3], np.float32)
+    cs = np.array([1.5, -0.25, 3.0, 1.0, -1.0, 0.5], np.float32)
+    S = oracle.abs_term_sum(a, sA, w4, ew, cs)
+    dec = {k: Fraction(float(v)) for k, v in enumerate(
+        torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().tolist())
+        if k & 0x7F != 0x7F}
+    for s in range(T):
+        for i in range(I):
+            ref = sum(abs(dec[int(a[s, h])] * dec[int(wn[h, i])]) *
+                      Fraction(2) ** (int(ew[h // 32, i]) - 127) for h in range(H))
+            ref *= abs(Fraction(float(sA[s]))) * abs(Fraction(float(cs[i])))
+            assert abs(S[s, i] - float(ref)) <= 1e-14 * float(ref)
+    # MX activation exponents enter inside the sum
+    ea = rng.integers(120, 134, (T, H // 32)).astype(np.uint8)
+    S2 = oracle.abs_term_sum(a, None, w4, ew, None, a_e8m0=ea)
+    for s in range(T):
+        i = s % I
+        ref = sum(abs(dec[int(a[s, h])] * dec[int(wn[h, i])]) *
+                  Fraction(2) ** (int(ew[h // 32, i]) + int(ea[s, h // 32]) - 254) for h in range(H))
+        assert abs(S2[s, i] - float(ref)) <= 1e-14 * float(ref)
+    # all codes non-negative: the sum of absolute terms is the contraction itself
+    ap, wp4 = a & 0x7F, w4 & 0x7F
+    b = codecs.f64_to_bf16(rng.standard_normal(I))
+    X, _ = oracle.project(ap, np.abs(sA), wp4, ew, np.abs(cs), b, num_heads=nq,
+                          num_kv_heads=nkv, head_dim=d)
+    Sp = oracle.abs_term_sum(ap, np.abs(sA), wp4, ew, np.abs(cs))
+    assert np.allclose(Sp, X - codecs.bf16_to_f64(b)[None, :], rtol=1e-13, atol=0)
+    # triangle inequality on signed codes
+    X, _ = oracle.project(a, sA, w4, ew, cs, b, num_heads=nq, num_kv_heads=nkv, head_dim=d)
+    assert (S >= np.abs(X - codecs.bf16_to_f64(b)[None, :]) * (1 - 1e-13)).all()
