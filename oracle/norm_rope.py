@@ -4,8 +4,8 @@
 [QKV-CTE] "Design 1)", step b: inv_rms = rsqrt(sum / (n_heads * d_head * tp) + eps) per token,
 for Q and for K (tp = 1 here: every head is local).  Each segment uses its own head count.
 Step c: re-read each token's Q / K as stored, multiply by the segment-wide per-channel gamma
-(``[1, n_heads * d_head]``, "Interface") and by inv_rms, write back in place; V is never normed
-and never re-read.
+(``[1, n_heads * d_head]``, "Interface") and by inv_rms, store the result over the
+input; V is never normed and never re-read.
 [QKV-CTE] "Design 2)": the norm precedes RoPE; rotate-half pairs lane j with lane j + d/2 and
 out = (x * inv_rms) * cos + [-x_hi, x_lo] * inv_rms * sin, with the per-position cos / sin row
 shared by every head.  The x in that formula is read here as the gamma-scaled value, i.e.

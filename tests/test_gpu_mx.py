@@ -25,9 +25,10 @@ def _blocky_activation(T, H, seed, spread=2):
     """N(0,1) rows with a random power of two (2^-spread .. 2^spread) per 32-element block and
     per-row gains in [0.5, 2], a zero block and a tiny block.  The spread keeps the exponents of
     neighbouring blocks apart (a misplaced exponent is off by a power of two) without the heavy
-    cancellation that wide spreads produce: one FP8 MFMA sums its 64 products to about 2^-12 of
-    their absolute sum (measured), so outputs that cancel to a small fraction of their terms'
-    sum fall outside the bf16 tolerance on any input encoding."""
+    cancellation that wide spreads produce: one FP8 MFMA sums its 64 products only to a small
+    fraction of their absolute sum, so outputs that cancel below that fraction fall outside the
+    plain bf16 tolerance on any input encoding.  The wide spreads (2^+-6 per block, row gains
+    10^+-2) are checked in test_gpu_accumulation.py against the tolerance plus that bound."""
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((T, H)).astype(np.float32)
     x *= np.ldexp(1.0, rng.integers(-spread, spread + 1, (T, H // 32))).repeat(32, axis=1).astype(np.float32)

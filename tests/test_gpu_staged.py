@@ -194,8 +194,9 @@ def _check_exp_padding(eimg, T, H):
 def _blocky(T, H, seed, spread=6):
     """N(0,1) rows with a random power of two in 2^-spread .. 2^spread per 32-element block, a
     zero block and a tiny block.  The projection tests use spread 2: one FP8 MFMA sums its 64
-    products to about 2^-12 of their absolute sum, so wide spreads produce outputs that cancel
-    below the bf16 tolerance on any encoding (the encoder tests use the wide spread)."""
+    products only to a small fraction of their absolute sum, so wide spreads produce outputs that
+    cancel below the plain bf16 tolerance on any encoding (the encoder tests use the wide spread;
+    test_gpu_accumulation.py checks wide spreads against the tolerance plus that bound)."""
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((T, H)).astype(np.float32)
     x *= np.ldexp(1.0, rng.integers(-spread, spread + 1, (T, H // 32))).repeat(32, axis=1).astype(np.float32)
