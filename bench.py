@@ -8,8 +8,12 @@ T = 75600 tokens (21 x 45 x 80 grid), H = 5120, 40 Q + 40 KV heads x 128 (I = 15
 
 Prints ONE JSON line.  ``value`` is the projection's algorithmic TFLOP/s over the whole step
 (2 * T * H * I / step time).  Per-kernel durations come from HIP events recorded on the stream
-the library launches on, averaged over the timed steps.  ``cpu_baseline`` times the CPU oracle
-(NumPy, fp64) on a bounded row sample of the same workload on this host.
+the library launches on, averaged over the timed steps.  ``configs`` times every other workload
+in the same run (the tiny, moderate and full-video self-attention projections with their norm +
+RoPE pass, the moderate one also with a 2 GiB last-level-cache flush between steps, and the
+cross-attention's three separate projections).  ``cpu_baseline`` times the CPU oracle (NumPy,
+fp64) on a bounded row sample of the same workload on this host.  The SHA-256 prefix of every
+generated input buffer is part of ``config``.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5|3|2] [--act rowmx|mx] [--headnorm none|rms|ln]
                     [--layout bsd|nbsd] [--no-cpu-baseline]
@@ -162,7 +166,10 @@ def parse():
     ap.add_argument("--headnorm", choices=["none", "rms", "ln"], default="none",
                     help="per-head qk-norm (RMS_NORM / LAYER_NORM) + RoPE fused into the projection's "
                          "epilogue instead of the across-heads norm pass (ROW_MX activations)")
-    ap.add_argument("--cpu-rows", type=int, default=8192)
+    ap.add_argument("--cpu-rows", type=int, default=16384)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the block that times every other workload (C1-C4, C2 also with a "
+                         "MALL flush) after the headline run")
     ap.add_argument("--graph", action="store_true",
                     help="also capture one step into a HIP graph and time --steps replays of it "
                          "(stages.graph_ms_per_step)")
@@ -195,19 +202,27 @@ def gen_inputs(cid, dev):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     inp = {"p": p, "producer": cfg.producer}
+    digests = {}
+
+    def keep(name, a):                 # SHA-256 prefix of every generated host buffer
+        digests[name] = synth.digest(a)
+        return a
+
     if cfg.producer:
         hid, res, gam = synth.producer_inputs(cid, p.T, p.H)
-        inp.update(hid=bf(hid), res=bf(res), pgamma=bf(gam))
+        inp.update(hid=bf(keep("hidden", hid)), res=bf(keep("residual", res)),
+                   pgamma=bf(keep("producer_gamma", gam)))
         del hid, res
     else:
-        inp["x"] = dv(synth.activation(p))
-    inp["w"] = dv(synth.weight(p))
-    inp["bias"] = bf(synth.bias_bf16(p))
-    inp["gq"] = bf(synth.gamma_bf16(p, "q"))
-    inp["gk"] = bf(synth.gamma_bf16(p, "k"))
+        inp["x"] = dv(keep("activation", synth.activation(p)))
+    inp["w"] = dv(keep("weight", synth.weight(p)))
+    inp["bias"] = bf(keep("bias", synth.bias_bf16(p)))
+    inp["gq"] = bf(keep("q_gamma", synth.gamma_bf16(p, "q")))
+    inp["gk"] = bf(keep("k_gamma", synth.gamma_bf16(p, "k")))
     cos, sin = synth.rope_tables(p)
-    inp["cos"], inp["sin"] = dv(cos), dv(sin)
+    inp["cos"], inp["sin"] = dv(keep("cos", cos)), dv(keep("sin", sin))
     inp["gen_s"] = time.time() - t0
+    inp["sha256"] = digests
     return inp
 
 
@@ -408,6 +423,7 @@ def run_gpu(args):
         "flops": flops,
         "bytes": nbytes,
         "gen_s": inp["gen_s"],
+        "sha256": inp["sha256"],
         "p": p,
         "producer": inp["producer"],
         "mx": mx,
@@ -601,7 +617,56 @@ def run_gpu_separate(args):
         "stages": {"ms": stages, "ms_median_min": stats, **rates},
         "ceilings": None, "cpu_baseline": None,
     }
-    print(json.dumps(line), flush=True)
+    return line
+
+
+def _compact(r):
+    """The per-workload figures of one run_gpu result."""
+    p = r["p"]
+    d = {"T": p.T, "H": p.H, "I": p.I,
+         "step_ms": r["ms_per_step"],
+         "projection_ms": r["stage_ms"]["projection"],
+         "projection_tflops": r["projection_tflops"],
+         "projection_frac_of_peak": r["projection_tflops"] / PEAK_MXFP8_TFLOPS,
+         "norm_rope_ms": r["stage_ms"]["norm_rope"],
+         "norm_rope_gbs": r["norm_rope_gbs"],
+         "norm_rope_hbm_frac": (r["norm_rope_gbs"] / PEAK_HBM_GBS) if r["norm_rope_gbs"] else None}
+    return d
+
+
+def run_config_block(args):
+    """Every other workload, measured in the same run with the same library calls as their own
+    ``--config N`` runs: the tiny (C1), moderate (C2) and full-video (C3) self-attention
+    projections with the norm + RoPE pass (activations quantised once, outside the step), C2
+    again with a 2 GiB scratch write between steps (so no step finds the previous one's data
+    in the 256 MB last-level cache), and the cross-attention's three separate projections (C4)."""
+    steps, warm = max(5, min(args.steps, 10)), 2
+    block = {}
+    for cid, flush in ((1, 0), (2, 0), (2, 2 << 30), (3, 0)):
+        a = argparse.Namespace(**vars(args))
+        a.config, a.steps, a.warmup, a.flush_mall, a.graph = cid, steps, warm, flush, False
+        r = _compact(run_gpu(a))
+        if flush:
+            block["C2"]["with_mall_flush_2GiB"] = r
+        else:
+            block[f"C{cid}"] = r
+        log(f"config block: C{cid}{' (MALL flush)' if flush else ''}: projection "
+            f"{r['projection_tflops']:.0f} TFLOP/s, norm {r['norm_rope_gbs']:.0f} GB/s")
+    a = argparse.Namespace(**vars(args))
+    a.config, a.steps, a.warmup = 4, steps, warm
+    line = run_gpu_separate(a)
+    st = line["stages"]
+    block["C4"] = {"step_ms": line["ms_per_step"], "calls": line["config"]["calls"],
+                   "ms": st["ms"],
+                   **{k: v for k, v in st.items() if k.endswith("_tflops") or k.endswith("_gbs")},
+                   **{k[:-len("_tflops")] + "_frac_of_peak": v / PEAK_MXFP8_TFLOPS
+                      for k, v in st.items() if k.endswith("_projection_tflops")},
+                   **{k[:-len("_gbs")] + "_hbm_frac": v / PEAK_HBM_GBS
+                      for k, v in st.items() if k.endswith("_norm_gbs")}}
+    block["note"] = (f"{steps} timed steps after {warm} warm-ups per workload; projection = the "
+                     "staged ROW_MX call (counter reset + project_kernel + sum reduce), norm = "
+                     "the norm (+ RoPE) pass, each timed with HIP events on the library's stream")
+    return block
 
 
 def cpu_baseline(cid, rows_n):
@@ -644,6 +709,9 @@ def cpu_baseline(cid, rows_n):
     flops = 2.0 * rows_n * p.H * p.I
     nb = algorithmic_bytes(dataclasses.replace(p, T=rows_n), cfg.producer)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "cores_note": "BLAS threads of the fp64 contraction (the oracle's only threaded "
+                          "stage; the rest runs on one core)",
+            "host_cores_available": len(os.sched_getaffinity(0)),
             "kind": "oracle", "blas": blas,
             "stages": {"producer_or_quantise_s": t1 - t0,
                        "producer_gbs": (nb["producer"] / (t1 - t0) / 1e9) if cfg.producer else None,
@@ -667,7 +735,7 @@ def main():
                                    "are not part of this benchmark)"}))
         sys.exit(2)
     if synth_configs_separate(args.config):
-        run_gpu_separate(args)
+        print(json.dumps(run_gpu_separate(args)), flush=True)
         return
     r = run_gpu(args)
     p = r["p"]
@@ -681,6 +749,10 @@ def main():
         if r["producer_gbs"]:
             ceil["producer_frac_of_copy"] = r["producer_gbs"] / ceil["hbm_copy_gbs"]
         log(f"ceilings: {ceil}")
+    block = None
+    if not args.no_configs and args.config == 5 and args.layout == "bsd" and not r["mx"] \
+            and r["headnorm"] == "none" and r["staged"]:
+        block = run_config_block(args)
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_rows} rows")
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.config, args.cpu_rows)
@@ -713,6 +785,7 @@ def main():
             "grid": list(p.grid) if p.grid else None, "layout": args.layout.upper().replace("NBSD", "NBSd"),
             "parallelism": "single GPU",
             "mall_flush_bytes_between_steps": args.flush_mall,
+            "inputs_sha256_16": r["sha256"],
         },
         "roofline": {
             "kernel": ("qkv_mx_project_staged (counter reset + project_kernel + ssq_reduce)"
@@ -746,6 +819,7 @@ def main():
             "producer_hbm_frac": (r["producer_gbs"] / PEAK_HBM_GBS) if r["producer_gbs"] else None,
         },
         "ceilings": ceil,
+        "configs": block,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -64,7 +64,15 @@ constexpr int kBufs = 4;                           // LDS stage buffers
 constexpr int kBufferRsrcWord3 = 0x00020000;        // buffer descriptor word 3 (gfx9 family)
 constexpr int kNonTemporal = 2;                    // buffer store cache policy: streaming
 constexpr uint32_t kDropOffset = 0x80000000u;      // outside any descriptor range (<= 2^31 - 1)
-constexpr int kTailStores = 8;                   // unconditional stores ending an epilogue
+// Unconditional stores ending an epilogue.  The next tile waits with vmcnt(kTailStores), i.e.
+// for everything but those stores, which is its DMAs only if vector memory operations complete
+// in issue order.  LLVM's AMDGPU memory-model documentation (AMDGPUUsage, memory model of the
+// GFX9 family including GFX90A/GFX942) states that vector memory operations report completion
+// to the wavefront in execution order, the exception being FLAT instructions that access LDS
+// memory; the DMAs here are global (not FLAT) loads and the stores buffer stores.  The
+// backend's own wait insertion relies on the same order (a load followed by two stores is
+// waited for with vmcnt(2) before the load's value is used, as compiled for gfx950).
+constexpr int kTailStores = 8;
 constexpr int kDmaPerStage = 8;                    // per wave: 4 (weight) + 4 (activation)
                                                    // (+ 2 exponent DMAs every 4th stage)
 

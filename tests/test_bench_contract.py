@@ -52,3 +52,16 @@ def test_traffic_record_is_tied_to_the_projection_sources():
     if rec["kernel_src_sha256_16"] == digest:
         assert bench.measured_traffic(bench.STAGED_KERNELS) == pytest.approx(
             rec["hbm_bytes_per_call"])
+
+
+def test_config_block_entry_divides_by_the_published_peaks():
+    """One workload's entry of the per-config block: projection TFLOP/s against 5.0 PFLOP/s,
+    norm GB/s against 8 TB/s, nothing recomputed from other fields."""
+    p = synth.CONFIGS[2].calls[0]
+    r = {"p": p, "ms_per_step": 0.33, "stage_ms": {"projection": 0.28, "norm_rope": 0.04},
+         "projection_tflops": 2300.0, "norm_rope_gbs": 4400.0}
+    c = bench._compact(r)
+    assert (c["T"], c["H"], c["I"]) == (4096, 5120, 15360)
+    assert c["projection_frac_of_peak"] == pytest.approx(2300.0 / 5000.0)
+    assert c["norm_rope_hbm_frac"] == pytest.approx(4400.0 / 8000.0)
+    assert c["projection_ms"] == 0.28 and c["norm_rope_ms"] == 0.04
