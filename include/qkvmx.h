@@ -273,6 +273,29 @@ qkvmx_status qkv_rowmx_project_staged(const uint8_t* act_image, size_t image_byt
                                       uint16_t* out, float* ssq, void* workspace,
                                       size_t ws_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, serving loops
+ * or harnesses that forbid hipMalloc): qkv_rowmx_project_staged without the workspace
+ * argument.  The projection's scratch (tile counters, sum-of-squares partials, split planes)
+ * lives in a static device array of qkvmx_noalloc_scratch_bytes() bytes (80 MiB) that every
+ * GPU the library runs on holds until the process ends; the call allocates nothing (no
+ * hipMalloc / hipFree, no allocating library routine) and launches the same kernels, so out
+ * and ssq are bit for bit those of qkv_rowmx_project_staged.  The counters the kernels need
+ * zeroed are cleared by a kernel on every call; nothing else is read before it is written.
+ *   Errors: QKVMX_ERR_WORKSPACE when qkv_staged_workspace_bytes(T, I) exceeds the scratch
+ *   (checked on the host before any HIP call); QKVMX_ERR_HIP if the scratch's device address
+ *   cannot be obtained (looked up once per device, with that device current, on its first
+ *   call).  Other arguments, layouts and errors as qkv_rowmx_project_staged.
+ *   All calls on one GPU share its scratch: calls that overlap on one GPU (concurrent streams)
+ *   race and must not be issued. */
+size_t qkvmx_noalloc_scratch_bytes(void);
+qkvmx_status qkv_rowmx_project_staged_noalloc(const uint8_t* act_image, size_t image_bytes,
+                                              const float* row_scale, const void* w_packed,
+                                              const float* w_channel_scale, const uint16_t* bias,
+                                              int64_t T, int64_t H, int32_t num_heads,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              int32_t layout, uint16_t* out, float* ssq,
+                                              hipStream_t stream);
+
 /* Pass 1 with the upstream per-head qk-norm and rotate-half RoPE fused into the epilogue
  * ([QKV-CTE] "Upstream behavior": an optional per-head qk-norm (RMS_NORM / LAYER_NORM) and
  * rotate-half RoPE applied as each finished result leaves the accumulators, with the dequant

@@ -26,6 +26,7 @@ __all__ = [
     "qkv_staged_workspace_bytes", "qkv_rowmx_project_staged", "mfma_rate_probe",
     "qkv_act_exp_image_bytes", "mx_block_quantize_staged", "rmsnorm_mx_block_quantize_staged",
     "qkv_mx_project_staged", "projection_k_chunks", "qkv_rowmx_project_headnorm_staged",
+    "qkv_rowmx_project_staged_noalloc", "noalloc_scratch_bytes",
 ]
 
 
@@ -383,6 +384,30 @@ def qkv_rowmx_project_staged(act_image, row_scale, w_packed, out, *, H: int, num
                                           num_heads, num_kv_heads, head_dim, layout, _ptr(out),
                                           _ptr(ssq), ws_ptr, ws_n, _stream(stream)),
            "qkv_rowmx_project_staged")
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the static device scratch behind qkv_rowmx_project_staged_noalloc."""
+    return int(lib().qkvmx_noalloc_scratch_bytes())
+
+
+def qkv_rowmx_project_staged_noalloc(act_image, row_scale, w_packed, out, *, H: int,
+                                     num_heads: int, num_kv_heads: int, head_dim: int,
+                                     channel_scale=None, bias=None, ssq=None,
+                                     layout: int = LAYOUT_BSD, stream=None):
+    """qkv_rowmx_project_staged without a workspace: the library's static per-GPU scratch
+    holds the projection's scratch, so the call allocates nothing.  Calls that overlap on one
+    GPU race on that scratch."""
+    _need(row_scale, "qkv_rowmx_project_staged_noalloc: row_scale", "f32")
+    T = row_scale.numel()
+    I = _width(num_heads, num_kv_heads, head_dim)
+    _need(act_image, "qkv_rowmx_project_staged_noalloc: act_image", None)
+    _check_projection_io("qkv_rowmx_project_staged_noalloc", T, H, I, w_packed, channel_scale,
+                         bias, out, ssq)
+    _check(lib().qkv_rowmx_project_staged_noalloc(
+        _ptr(act_image), _nbytes(act_image), _ptr(row_scale), _ptr(w_packed), _ptr(channel_scale),
+        _ptr(bias), T, H, num_heads, num_kv_heads, head_dim, layout, _ptr(out), _ptr(ssq),
+        _stream(stream)), "qkv_rowmx_project_staged_noalloc")
 
 
 def qkv_rowmx_project_headnorm(packed_a, w_packed, out, *, H: int, num_heads: int,

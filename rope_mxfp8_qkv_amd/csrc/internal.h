@@ -130,6 +130,14 @@ inline size_t staged_workspace_total_bytes(int64_t T, int64_t I) {
   return staged_counters_offset(T, I) + kCounterBytes + split_planes_bytes(T, I);
 }
 
+// The entry point that allocates nothing (qkv_rowmx_project_staged_noalloc) keeps the staged
+// projection's workspace in a static device array of this size (one per GPU, held until the
+// process ends): 80 MiB holds the full-video call's 69.2 MB (120 partials x 75600 tokens) and
+// a split 512-token context call's planes (30.2 MB).
+constexpr size_t kNoAllocScratchBytes = (size_t)80 << 20;
+// Device address of the current device's static scratch array (project_noalloc.hip).
+hipError_t noalloc_scratch(void** out);
+
 hipError_t launch_mx_weight_quantize(const float* w, int64_t H, int64_t I, uint8_t* codes,
                                      uint8_t* e8m0, hipStream_t s);
 hipError_t launch_weight_prepack(const uint8_t* codes, const uint8_t* e8m0, int64_t H, int64_t I,

@@ -322,6 +322,48 @@ qkvmx_status qkv_rowmx_project_staged(const uint8_t* act_image, size_t image_byt
                                           (uint8_t*)workspace, stream), fn);
 }
 
+size_t qkvmx_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+qkvmx_status qkv_rowmx_project_staged_noalloc(const uint8_t* act_image, size_t image_bytes,
+                                              const float* row_scale, const void* w_packed,
+                                              const float* w_channel_scale, const uint16_t* bias,
+                                              int64_t T, int64_t H, int32_t num_heads,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              int32_t layout, uint16_t* out, float* ssq,
+                                              hipStream_t stream) {
+  const char* fn = "qkv_rowmx_project_staged_noalloc";
+  if (!act_image || !row_scale || !w_packed || !out) return fail(QKVMX_ERR_NULL, "%s: null pointer", fn);
+  if (T <= 0 || H <= 0 || H % 32) return fail(QKVMX_ERR_SHAPE, "%s: need T > 0, H %% 32 == 0", fn);
+  if (num_heads < 1 || num_kv_heads < 0 || head_dim <= 0 || head_dim % 16)
+    return fail(QKVMX_ERR_SHAPE, "%s: need num_heads >= 1, num_kv_heads >= 0, head_dim %% 16 == 0", fn);
+  if (layout != QKVMX_LAYOUT_BSD && layout != QKVMX_LAYOUT_NBSD)
+    return fail(QKVMX_ERR_ARG, "%s: layout must be QKVMX_LAYOUT_BSD or QKVMX_LAYOUT_NBSD", fn);
+  const int64_t I = (int64_t)(num_heads + 2 * (int64_t)num_kv_heads) * head_dim;
+  if (I * 2 * 256 >= kMaxOffset)
+    return fail(QKVMX_ERR_UNSUPPORTED, "%s: I must be < 2^22", fn);
+  if (staged_workspace_total_bytes(T, I) > kNoAllocScratchBytes)
+    return fail(QKVMX_ERR_WORKSPACE,
+                "%s: T = %lld, I = %lld needs %zu bytes of scratch; the static scratch holds %zu "
+                "(use qkv_rowmx_project_staged with a workspace)", fn, (long long)T,
+                (long long)I, staged_workspace_total_bytes(T, I), kNoAllocScratchBytes);
+  if (image_bytes < act_image_bytes(T, H))
+    return fail(QKVMX_ERR_SHAPE, "%s: image_bytes %zu < %zu", fn, image_bytes, act_image_bytes(T, H));
+  if (layout == QKVMX_LAYOUT_NBSD && 2 * ((256 + (int64_t)head_dim) * T + 257 * (int64_t)head_dim) >= kMaxOffset)
+    return fail(QKVMX_ERR_UNSUPPORTED, "%s: NBSd needs 2 ((256 + head_dim) T + 257 head_dim) < 2^31", fn);
+  if (!aligned(act_image, 256) || !aligned(row_scale, 4) || !aligned(w_packed, 256) ||
+      (w_channel_scale && !aligned(w_channel_scale, 16)) || (bias && !aligned(bias, 8)) ||
+      !aligned(out, 16) || (ssq && !aligned(ssq, 8)))
+    return fail(QKVMX_ERR_ALIGN, "%s: alignment (act_image 256, row_scale 4, w_packed 256, channel scale 16, bias 8, out 16, ssq 8)", fn);
+  void* scratch = nullptr;
+  const qkvmx_status st = hip_status(noalloc_scratch(&scratch), fn);
+  if (st != QKVMX_OK) return st;
+  const int64_t Iq = (int64_t)num_heads * head_dim, Ik = (int64_t)num_kv_heads * head_dim;
+  return hip_status(launch_project_staged(act_image, row_scale, (const uint8_t*)w_packed,
+                                          w_channel_scale, bias, T, H, I, Iq, Ik, head_dim,
+                                          layout == QKVMX_LAYOUT_NBSD, out, ssq,
+                                          (uint8_t*)scratch, stream), fn);
+}
+
 // Checks shared by the two per-head qk-norm projections (norm kind, shapes, the head geometry
 // the fused epilogue supports, layout, gamma / beta / table pairing, eps); QKVMX_OK if they hold.
 static qkvmx_status check_headnorm(const char* fn, int64_t T, int64_t H, int32_t num_heads,

@@ -207,6 +207,37 @@ def test_staged_path_validation():
     assert L.rmsnorm_mx_quantize_staged(None, None, P, 1e-6, 4, 256, 0, None, P, 1 << 20, P, None) == 1
 
 
+def _stproj_na(L, **kw):
+    a = dict(act_image=P, image_bytes=1 << 30, row_scale=P, w_packed=P, w_channel_scale=None,
+             bias=None, T=4, H=256, num_heads=2, num_kv_heads=2, head_dim=64, layout=0, out=P,
+             ssq=None, stream=None)
+    a.update(kw)
+    return L.qkv_rowmx_project_staged_noalloc(*a.values())
+
+
+def test_noalloc_projection_validation():
+    """The entry point without a workspace: the same host checks as the staged projection, and
+    calls whose scratch would exceed the static array are refused before any HIP call."""
+    L = _lib()
+    cap = L.qkvmx_noalloc_scratch_bytes()
+    assert cap == 80 << 20
+    # the full-video call fits, with its 120 partials per token
+    assert L.qkv_staged_workspace_bytes(75600, 15360) <= cap
+    assert _stproj_na(L, act_image=None) == 1
+    assert _stproj_na(L, out=None) == 1
+    assert _stproj_na(L, H=100) == 2
+    assert _stproj_na(L, head_dim=40) == 2
+    assert _stproj_na(L, layout=2) == 4
+    assert _stproj_na(L, image_bytes=16384 * 4 - 1) == 2
+    assert _stproj_na(L, act_image=P + 16) == 3
+    assert _stproj_na(L, out=P + 2) == 3
+    # too large for the scratch: T = 90000 tokens at I = 15360 needs 120 * 90000 * 8 bytes
+    assert L.qkv_staged_workspace_bytes(90000, 15360) > cap
+    assert _stproj_na(L, T=90000, num_heads=40, num_kv_heads=40, head_dim=128) == 5
+    from rope_mxfp8_qkv_amd import _abi
+    assert "static scratch holds" in _abi.last_error()
+
+
 def test_mx_staged_validation():
     L = _lib()
     # exponent image: 296 token tiles x 20 supersteps x 256 rows x 2 dwords
