@@ -427,6 +427,19 @@ qkvmx_status qk_norm_rope_apply(uint16_t* qkv, const float* ssq, const uint16_t*
 qkvmx_status qkvmx_mfma_rate_probe(int32_t blocks, int32_t iters, int32_t random_operands,
                                    float* sink, uint64_t* clocks, hipStream_t stream);
 
+/* Check of the producers' E4M3 encoding (a measurement helper, not a step of the method).  The
+ * ROW_MX and MX producers form their codes with the hardware's packing conversion after a clamp
+ * to [-448, 448]; this launches one kernel that compares that path with the library's software
+ * round-to-nearest-even saturating encoder on every finite fp32 value (all 2^32 bit patterns).
+ *   counts     device uint64 [3], zeroed by the caller: counts[0] += values whose codes differ,
+ *              counts[1] += finite values compared (2^32 - 2^24: every pattern but the 2^24
+ *              infinities and NaNs),
+ *              counts[2] = number of mismatches recorded (at most 8 kept).
+ *   first_bad  device uint32 [8] or NULL: bit patterns of the first mismatching values.
+ * Asynchronous on `stream`; QKVMX_ERR_NULL / QKVMX_ERR_ALIGN for bad pointers. */
+qkvmx_status qkvmx_e4m3_convert_check(unsigned long long* counts, uint32_t* first_bad,
+                                      hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,7 @@ __all__ = [
     "qkv_staged_workspace_bytes", "qkv_rowmx_project_staged", "mfma_rate_probe",
     "qkv_act_exp_image_bytes", "mx_block_quantize_staged", "rmsnorm_mx_block_quantize_staged",
     "qkv_mx_project_staged", "projection_k_chunks", "qkv_rowmx_project_headnorm_staged",
-    "qkv_rowmx_project_staged_noalloc", "noalloc_scratch_bytes",
+    "qkv_rowmx_project_staged_noalloc", "noalloc_scratch_bytes", "e4m3_convert_check",
 ]
 
 
@@ -494,3 +494,12 @@ def mfma_rate_probe(blocks: int, iters: int, random_operands: bool, sink, clocks
     _need(clocks, "mfma_rate_probe: clocks", "i64", numel=blocks * 2)
     _check(lib().qkvmx_mfma_rate_probe(blocks, iters, int(bool(random_operands)), _ptr(sink),
                                        _ptr(clocks), _stream(stream)), "qkvmx_mfma_rate_probe")
+
+
+def e4m3_convert_check(counts, first_bad=None, stream=None):
+    """The producers' hardware E4M3 conversion against the software encoder on every finite
+    fp32 value (include/qkvmx.h); ``counts`` int64 [3] zeroed, ``first_bad`` int32 [8] or None."""
+    _need(counts, "e4m3_convert_check: counts", "i64", numel=3)
+    _need(first_bad, "e4m3_convert_check: first_bad", "i32", numel=8, optional=True)
+    _check(lib().qkvmx_e4m3_convert_check(_ptr(counts), _ptr(first_bad), _stream(stream)),
+           "qkvmx_e4m3_convert_check")

@@ -69,6 +69,7 @@ SIGNATURES = {
     "qkv_rowmx_project_staged_noalloc": (c_i32, [c_vp, c_sz, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64,
                                                  c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
     "qkvmx_mfma_rate_probe": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
+    "qkvmx_e4m3_convert_check": (c_i32, [c_vp, c_vp, c_vp]),
     "qk_norm_rope_apply": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_i32, c_i32,
                                    c_f, c_u32, c_i32, c_vp]),
 }

@@ -6,6 +6,11 @@
 // quantised activations and weights are) or all zero; the two differ in how much the operand
 // bits toggle, hence in power, hence in the clock the chip sustains.  Each block also reports
 // its elapsed core-clock cycles and 100 MHz reference ticks, from which the clock follows.
+//
+// Also the exhaustive check of the producers' E4M3 encoding: the hardware packing conversion
+// after a clamp to +-448 against the software round-to-nearest-even encoder, on every finite
+// fp32 value.
+#include "device_common.h"
 #include "internal.h"
 
 namespace qkvmx {
@@ -63,7 +68,43 @@ __global__ void __launch_bounds__(256, 1) mfma_rate_kernel(int iters, unsigned s
   }
 }
 
+// Every 32-bit pattern p (4 consecutive patterns per thread and step): for each finite fp32
+// value of the four, the hardware path (e4m3x4) and the software encoder (f32_to_e4m3) must give
+// the same code byte.  counts[0] += mismatching values, counts[1] += finite values compared;
+// the first 8 mismatching patterns go to first_bad (if given).
+__global__ void __launch_bounds__(256) e4m3_check_kernel(unsigned long long* __restrict__ counts,
+                                                         uint32_t* __restrict__ first_bad) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x * 4;
+  unsigned long long bad = 0, seen = 0;
+  for (uint64_t base = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; base < (1ull << 32);
+       base += stride) {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float((uint32_t)(base + i));
+    const uint32_t hw = e4m3x4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!__builtin_isfinite(v[i])) continue;
+      ++seen;
+      if (((hw >> (8 * i)) & 0xFFu) != f32_to_e4m3(v[i])) {
+        ++bad;
+        if (first_bad) {
+          const unsigned long long slot = atomicAdd(&counts[2], 1ull);
+          if (slot < 8) first_bad[slot] = (uint32_t)(base + i);
+        }
+      }
+    }
+  }
+  if (bad) atomicAdd(&counts[0], bad);
+  atomicAdd(&counts[1], seen);
+}
+
 }  // namespace
+
+hipError_t launch_e4m3_check(unsigned long long* counts, uint32_t* first_bad, hipStream_t s) {
+  hipLaunchKernelGGL(e4m3_check_kernel, dim3(1024), dim3(256), 0, s, counts, first_bad);
+  return hipGetLastError();
+}
 
 hipError_t launch_mfma_rate(int blocks, int iters, bool random_operands, float* sink,
                             uint64_t* clocks, hipStream_t s) {

@@ -36,4 +36,17 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   return (a < 0.015625f ? sub : nrm) | sign;
 }
 
+// Four E4M3 codes (round to nearest even, saturating at +-448, sign kept) packed little-endian
+// (byte i = code of the i-th argument), by the hardware's packing conversion after a clamp to
+// [-448, 448] (the conversion itself does not saturate).  Equal to f32_to_e4m3 on every finite
+// fp32 input: qkvmx_e4m3_convert_check compares the two on all 2^32 bit patterns.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const float lo = -448.0f, hi = 448.0f;
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, lo, hi),
+                                          __builtin_amdgcn_fmed3f(b, lo, hi), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(c, lo, hi),
+                                      __builtin_amdgcn_fmed3f(d, lo, hi), w, true);
+  return (uint32_t)w;
+}
+
 }  // namespace qkvmx

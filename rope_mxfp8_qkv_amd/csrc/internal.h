@@ -138,6 +138,7 @@ constexpr size_t kNoAllocScratchBytes = (size_t)80 << 20;
 // Device address of the current device's static scratch array (project_noalloc.hip).
 hipError_t noalloc_scratch(void** out);
 
+hipError_t launch_e4m3_check(unsigned long long* counts, uint32_t* first_bad, hipStream_t s);
 hipError_t launch_mx_weight_quantize(const float* w, int64_t H, int64_t I, uint8_t* codes,
                                      uint8_t* e8m0, hipStream_t s);
 hipError_t launch_weight_prepack(const uint8_t* codes, const uint8_t* e8m0, int64_t H, int64_t I,

@@ -576,6 +576,15 @@ qkvmx_status qk_norm_rope_apply(uint16_t* qkv, const float* ssq, const uint16_t*
                                      layout == QKVMX_LAYOUT_NBSD, stream), "qk_norm_rope_apply");
 }
 
+qkvmx_status qkvmx_e4m3_convert_check(unsigned long long* counts, uint32_t* first_bad,
+                                      hipStream_t stream) {
+  const char* fn = "qkvmx_e4m3_convert_check";
+  if (!counts) return fail(QKVMX_ERR_NULL, "%s: counts is required", fn);
+  if (!aligned(counts, 8) || (first_bad && !aligned(first_bad, 4)))
+    return fail(QKVMX_ERR_ALIGN, "%s: counts 8-byte, first_bad 4-byte aligned", fn);
+  return hip_status(launch_e4m3_check(counts, first_bad, stream), fn);
+}
+
 qkvmx_status qkvmx_mfma_rate_probe(int32_t blocks, int32_t iters, int32_t random_operands,
                                    float* sink, uint64_t* clocks, hipStream_t stream) {
   const char* fn = "qkvmx_mfma_rate_probe";

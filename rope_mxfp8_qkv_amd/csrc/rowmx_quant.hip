@@ -109,11 +109,11 @@ __device__ __forceinline__ void encode_store(const float (&y)[kCpt][kChunk], flo
     if (c < nchunks) {
       uint32_t lo = 0, hi = 0;
       if (s > 0.0f) {
+        float q[kChunk];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lo |= f32_to_e4m3((float)((double)y[k][e] * rinv)) << (8 * e);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          hi |= f32_to_e4m3((float)((double)y[k][4 + e] * rinv)) << (8 * e);
+        for (int e = 0; e < kChunk; ++e) q[e] = (float)((double)y[k][e] * rinv);
+        lo = e4m3x4(q[0], q[1], q[2], q[3]);
+        hi = e4m3x4(q[4], q[5], q[6], q[7]);
       }
       *reinterpret_cast<u32x2_a4*>(dst.chunk(c)) = u32x2_a4{lo, hi};
     } else if (c < dst.pad_chunks()) {
@@ -237,6 +237,130 @@ __device__ __forceinline__ void normed_row(const uint16_t* __restrict__ hid,
   }
 }
 
+// One wavefront per row (rows of up to 512 NC elements): lane l owns the 8-element chunks
+// l, l + 64, .., l + 64 (NC - 1), so each load instruction of the wavefront covers 1 KiB
+// contiguous, and both row reductions (the fp64 sum of squares and the maximum) are butterfly
+// exchanges inside the wavefront: no LDS, no block barrier between a row's loads and its
+// stores.  Arithmetic, rounding and the reduction's fixed order (the same butterfly on every
+// lane, so every lane holds the identical sum) follow normed_row / encode_store.
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+constexpr int kRowsPerWaveBlock = 4;       // rows (wavefronts) per 256-thread block
+
+template <bool RES, bool STAGED, int NC>
+__global__ void __launch_bounds__(64 * kRowsPerWaveBlock) rmsnorm_quantize_wave_kernel(
+    const uint16_t* __restrict__ hid, const uint16_t* __restrict__ res,
+    const uint16_t* __restrict__ gamma, float eps, int64_t T, int64_t H, int64_t Hu,
+    uint16_t* __restrict__ res_out, uint8_t* __restrict__ out, float* __restrict__ row_scale,
+    int KS, int64_t rows) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerWaveBlock + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int64_t nchunks = H / kChunk;
+  if (STAGED && row >= T) {                 // rows past T up to the tile end: zero codes
+    const StagedRow d = staged_row(out, nullptr, row, KS);
+    for (int64_t c = lane; c < d.padded; c += 64)
+      *reinterpret_cast<u32x2_a4*>(d.chunk(c)) = u32x2_a4{0u, 0u};
+    return;
+  }
+  // all of the row's loads first (2 NC x 16 bytes per lane in flight)
+  uint4 hv[NC], rv[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int64_t c = lane + 64 * k;
+    if (c < nchunks) {
+      hv[k] = ntload16(hid + row * H + c * kChunk);
+      if (RES) rv[k] = ntload16(res + row * H + c * kChunk);
+    }
+  }
+  float y[NC][kChunk];
+  double ss = 0.0;
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int64_t c = lane + 64 * k;
+#pragma unroll
+    for (int e = 0; e < kChunk; ++e) y[k][e] = 0.0f;
+    if (c < nchunks) {
+      if (RES) {
+        const uint32_t hw[4] = {hv[k].x, hv[k].y, hv[k].z, hv[k].w};
+        const uint32_t rw[4] = {rv[k].x, rv[k].y, rv[k].z, rv[k].w};
+        uint32_t ow[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // r = bf16_RNE(fp32 + fp32): one fp32 rounding, then one bf16 rounding
+          ow[e] = pack_bf16x2(bf16_to_f32(hw[e] & 0xFFFFu) + bf16_to_f32(rw[e] & 0xFFFFu),
+                              bf16_to_f32(hw[e] >> 16) + bf16_to_f32(rw[e] >> 16));
+          y[k][2 * e] = bf16_to_f32(ow[e] & 0xFFFFu);
+          y[k][2 * e + 1] = bf16_to_f32(ow[e] >> 16);
+        }
+        __builtin_nontemporal_store(u32x4_t{ow[0], ow[1], ow[2], ow[3]},
+                                    reinterpret_cast<u32x4_t*>(res_out + row * H + c * kChunk));
+      } else {
+        unpack8(hv[k], y[k]);
+      }
+#pragma unroll
+      for (int e = 0; e < kChunk; ++e) ss += (double)y[k][e] * (double)y[k][e];
+    }
+  }
+  ss = wave_sum(ss);
+  // inv = fp32(1 / sqrt(ss / Hu + eps)), sqrt and divide correctly rounded in fp64
+  const float inv = (float)(1.0 / sqrt(ss / (double)Hu + (double)eps));
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int64_t c = lane + 64 * k;
+    if (c < nchunks) {
+      float g[kChunk];
+      unpack8(reinterpret_cast<const uint4*>(gamma)[c], g);
+#pragma unroll
+      for (int e = 0; e < kChunk; ++e) {
+        y[k][e] = (y[k][e] * inv) * g[e];                       // two fp32 roundings
+        amax = fmaxf(amax, fabsf(y[k][e]));
+      }
+    }
+  }
+  amax = wave_max(amax);
+  // s = fl32(amax / 448); codes = E4M3 RNE saturating of fl32(y / s), formed as
+  // fl32(fl64(y * fl64(1 / s))) (exact: see encode_store); a zero row stores s = 0, zero codes
+  const float s = amax / 448.0f;
+  const double rinv = 1.0 / (double)s;
+  StagedRow sd{};
+  if (STAGED) sd = staged_row(out, row_scale, row, KS);
+  uint8_t* const prow = out + row * (H + 4);
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int64_t c = lane + 64 * k;
+    if (c < nchunks) {
+      uint32_t lo = 0, hi = 0;
+      if (s > 0.0f) {
+        float q[kChunk];
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) q[e] = (float)((double)y[k][e] * rinv);
+        lo = e4m3x4(q[0], q[1], q[2], q[3]);
+        hi = e4m3x4(q[4], q[5], q[6], q[7]);
+      }
+      *reinterpret_cast<u32x2_a4*>(STAGED ? sd.chunk(c) : prow + c * kChunk) = u32x2_a4{lo, hi};
+    }
+  }
+  if (STAGED) {                             // K-bytes from H to the stage end: zero codes
+    for (int64_t c = nchunks + lane; c < sd.padded; c += 64)
+      *reinterpret_cast<u32x2_a4*>(sd.chunk(c)) = u32x2_a4{0u, 0u};
+  }
+  if (lane == 0) {
+    if (STAGED) sd.scale(s);
+    else *reinterpret_cast<float*>(prow + H) = s;
+  }
+}
+
 template <bool RES, bool STAGED>
 __global__ void __launch_bounds__(1024) rmsnorm_quantize_kernel(
     const uint16_t* __restrict__ hid, const uint16_t* __restrict__ res,
@@ -291,10 +415,8 @@ __device__ __forceinline__ void mx_encode_codes(const float (&y)[kCpt][kChunk], 
     if (c < nchunks) {
       uint32_t lo = 0, hi = 0;
       if (m > 0.0f) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) lo |= f32_to_e4m3(y[k][e] * inv) << (8 * e);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hi |= f32_to_e4m3(y[k][4 + e] * inv) << (8 * e);
+        lo = e4m3x4(y[k][0] * inv, y[k][1] * inv, y[k][2] * inv, y[k][3] * inv);
+        hi = e4m3x4(y[k][4] * inv, y[k][5] * inv, y[k][6] * inv, y[k][7] * inv);
       }
       __builtin_nontemporal_store(u32x2_t{lo, hi}, reinterpret_cast<u32x2_t*>(chunk_at(c)));
       if ((c & 3) == 0) sh_e[c >> 2] = (uint8_t)E;
@@ -454,9 +576,41 @@ hipError_t launch_row_quantize_staged(const void* x, int dtype, int64_t T, int64
   return hipGetLastError();
 }
 
+// The fused ROW_MX producer, one wavefront per row, for rows of up to 512 NC elements (NC
+// chunks of 8 per lane): false (nothing launched) when H is wider than the widest instance.
+template <bool STAGED>
+bool launch_rmsnorm_quantize_wave(const uint16_t* hid, const uint16_t* res,
+                                  const uint16_t* gamma, float eps, int64_t T, int64_t H,
+                                  int64_t Hu, uint16_t* res_out, uint8_t* out, float* row_scale,
+                                  int KS, hipStream_t s) {
+  const int64_t rows = STAGED ? ceil_div(T, kTileM) * kTileM : T;
+  const dim3 grid((unsigned)ceil_div(rows, kRowsPerWaveBlock)), block(64 * kRowsPerWaveBlock);
+  const int64_t nc = ceil_div(H, (int64_t)64 * kChunk);
+#define QKVMX_WAVE_PRODUCER(N)                                                                   \
+  do {                                                                                           \
+    if (res)                                                                                     \
+      hipLaunchKernelGGL((rmsnorm_quantize_wave_kernel<true, STAGED, N>), grid, block, 0, s,     \
+                         hid, res, gamma, eps, T, H, Hu, res_out, out, row_scale, KS, rows);    \
+    else                                                                                         \
+      hipLaunchKernelGGL((rmsnorm_quantize_wave_kernel<false, STAGED, N>), grid, block, 0, s,    \
+                         hid, res, gamma, eps, T, H, Hu, res_out, out, row_scale, KS, rows);    \
+  } while (0)
+  if (nc <= 2) QKVMX_WAVE_PRODUCER(2);
+  else if (nc <= 4) QKVMX_WAVE_PRODUCER(4);
+  else if (nc <= 8) QKVMX_WAVE_PRODUCER(8);
+  else if (nc <= 10) QKVMX_WAVE_PRODUCER(10);
+  else if (nc <= 16) QKVMX_WAVE_PRODUCER(16);
+  else return false;
+#undef QKVMX_WAVE_PRODUCER
+  return true;
+}
+
 hipError_t launch_rmsnorm_quantize(const uint16_t* hid, const uint16_t* res, const uint16_t* gamma,
                                    float eps, int64_t T, int64_t H, int64_t Hu, uint16_t* res_out,
                                    uint8_t* packed, hipStream_t s) {
+  if (launch_rmsnorm_quantize_wave<false>(hid, res, gamma, eps, T, H, Hu, res_out, packed,
+                                          nullptr, 0, s))
+    return hipGetLastError();
   const dim3 grid((unsigned)T), block(block_threads(H));
   if (res)
     hipLaunchKernelGGL((rmsnorm_quantize_kernel<true, false>), grid, block, 0, s, hid, res,
@@ -471,8 +625,11 @@ hipError_t launch_rmsnorm_quantize_staged(const uint16_t* hid, const uint16_t* r
                                           const uint16_t* gamma, float eps, int64_t T, int64_t H,
                                           int64_t Hu, uint16_t* res_out, uint8_t* img,
                                           float* row_scale, hipStream_t s) {
-  const dim3 grid((unsigned)(ceil_div(T, kTileM) * kTileM)), block(block_threads(H));
   const int KS = (int)packed_stages(H);
+  if (launch_rmsnorm_quantize_wave<true>(hid, res, gamma, eps, T, H, Hu, res_out, img,
+                                         row_scale, KS, s))
+    return hipGetLastError();
+  const dim3 grid((unsigned)(ceil_div(T, kTileM) * kTileM)), block(block_threads(H));
   if (res)
     hipLaunchKernelGGL((rmsnorm_quantize_kernel<true, true>), grid, block, 0, s, hid, res,
                        gamma, eps, T, H, Hu, res_out, img, row_scale, KS);

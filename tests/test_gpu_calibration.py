@@ -26,3 +26,21 @@ def test_mfma_rate_probe_runs():
         assert np.isfinite(s).all()
         if not rnd:
             assert (s == 0).all()
+
+
+def test_hardware_e4m3_conversion_equals_software_encoder_on_every_fp32():
+    """The producers form their E4M3 codes with the hardware's packing conversion after a clamp
+    to +-448; on every finite fp32 value (2^32 - 2^24 bit patterns) that path must give the
+    same code byte as the software round-to-nearest-even saturating encoder, whose codes the
+    bit-exact producer tests compare with the oracle's."""
+    import torch
+    import rope_mxfp8_qkv_amd as q
+    dev = G.torch_dev()
+    counts = torch.zeros(3, dtype=torch.int64, device=dev)
+    first = torch.zeros(8, dtype=torch.int32, device=dev)
+    q.e4m3_convert_check(counts, first)
+    torch.cuda.synchronize()
+    c = counts.cpu().numpy()
+    assert int(c[1]) == 2 ** 32 - 2 ** 24
+    bad = first.cpu().numpy().view(np.uint32)[:min(int(c[2]), 8)]
+    assert int(c[0]) == 0, (int(c[0]), [hex(int(b)) for b in bad])
