@@ -10,9 +10,13 @@
 // the position-only tables across heads; each head costs two independent 16-byte loads of x
 // (plus gamma, an L1/L2 hit) and two 16-byte streaming stores.  inv_rms is folded into the gamma
 // multiply.  The two layouts differ only in how threads map to (token, head): see the kernels.
-// Blocks of 8 tokens (512 threads), ten heads' loads in flight per thread before their
-// stores, streaming loads and stores of x: the shape that moved the most bytes per second
-// in a sweep of block size, batch depth and cache policy on the in-place strided pattern.
+// Blocks of 4 tokens (256 threads), ten heads' loads in flight per thread before their
+// stores, streaming loads and stores of x, and the blocks visit the tokens from the last one
+// down: the projection writes its output token tile by token tile upwards, so the rows it
+// wrote last are still in the 256 MB last-level cache when this pass starts, and reading them
+// first finds them there instead of after the cache has turned over.  That order and block
+// shape moved the most bytes per second right after the projection in interleaved A/B runs at
+// the full video shape (blocks of 8, 16 and 2 tokens, batch depths 5 and 10, cached loads).
 #include "device_common.h"
 #include "internal.h"
 
@@ -21,7 +25,7 @@ namespace qkvmx {
 namespace {
 
 constexpr int kThreadsPerToken = 64;
-constexpr int kTokensPerBlock = 8;
+constexpr int kTokensPerBlock = 4;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -140,7 +144,9 @@ __device__ __forceinline__ void apply_token(const NormRopeArgs& a, int64_t token
 // (G = 64 / (d / 16) head groups), so one wave instruction covers G heads of one token row.
 __global__ void __launch_bounds__(kThreadsPerToken * kTokensPerBlock) norm_rope_kernel(
     const NormRopeArgs a) {
-  const int64_t token = (int64_t)blockIdx.x * kTokensPerBlock + (threadIdx.x / kThreadsPerToken);
+  // blocks from the last token down (see the file comment)
+  const int64_t token = (int64_t)(gridDim.x - 1 - blockIdx.x) * kTokensPerBlock +
+                        (threadIdx.x / kThreadsPerToken);
   if (token >= a.T) return;
   const int lane = threadIdx.x % kThreadsPerToken;
   const int cpd = a.d / 16;                 // chunks per head half-pair
@@ -165,7 +171,7 @@ __global__ void __launch_bounds__(kThreadsPerToken * kTokensPerBlock) norm_rope_
   const int lane = threadIdx.x % kThreadsPerToken, wave = threadIdx.x / kThreadsPerToken;
   const int slot = lane / cpd;
   if (slot >= tpw) return;                  // lanes past the last whole token (64 % cpd != 0)
-  const int64_t token = ((int64_t)blockIdx.x * kTokensPerBlock + wave) * tpw + slot;
+  const int64_t token = ((int64_t)(gridDim.x - 1 - blockIdx.x) * kTokensPerBlock + wave) * tpw + slot;
   if (token >= a.T) return;
   apply_token(a, token, (lane % cpd) * 8, 0, 1, [&](int h, bool is_k) {
     // head index in the output: Q heads first, then K heads (which follow all nq Q heads)
