@@ -160,11 +160,14 @@ __device__ __forceinline__ int fresh_lane() {
   return r;
 }
 
-// v + (v of lane ^ 32): the two lane halves' partial sums combined (ds_bpermute addressed from
-// a fresh lane index).
+// v + (v of lane ^ 32): the two lane halves' partial sums combined.  V_PERMLANE32_SWAP with
+// both operands v leaves, in every lane l, the pair (v[l % 32], v[l % 32 + 32]), so lane l and
+// lane l ^ 32 add the same two values in the same order (identical results) with one VALU
+// instruction instead of an LDS permute.
 __device__ __forceinline__ float add_xor32(float v) {
-  const int src = (fresh_lane() ^ 32) << 2;
-  return v + __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v)));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int N>
@@ -212,6 +215,10 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
   __shared__ __attribute__((aligned(16))) float lds_sa[2][kTileM];
   __shared__ __attribute__((aligned(16))) uint32_t lds_braw[2][kTileN / 2];
   __shared__ __attribute__((aligned(16))) float lds_bias[2][kTileN];
+  // per-head qk-norm: gamma of the Q and the K segment, then their LayerNorm beta (0 when
+  // absent), widened to fp32 once per kernel (head_dim <= 128; every head of a segment shares
+  // them, so each epilogue pass reads them from LDS instead of global memory)
+  __shared__ __attribute__((aligned(16))) float lds_hgb[kHead ? 4 : 1][kHead ? 128 : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -250,6 +257,14 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     return -1;
   };
   if (tid == 0) lds_tile[0] = claim((int)atomicAdd(&a.ctr[my_xcd], 1u));
+  if (kHead != 0) {
+    for (int i = tid; i < 4 * 128; i += kThreads) {
+      const int which = i >> 7, j = i & 127;
+      const uint16_t* src = which == 0 ? a.hq_gamma : which == 1 ? a.hk_gamma
+                          : which == 2 ? a.hq_beta : a.hk_beta;
+      lds_hgb[which][j] = (src && j < a.d) ? bf16_to_f32(src[j]) : 0.0f;
+    }
+  }
   __syncthreads();
   const int first_tile = __builtin_amdgcn_readfirstlane(lds_tile[0]);
   if (first_tile < 0) return;             // the whole block, nothing left
@@ -540,6 +555,26 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     const int hseg = kHead == 0 ? 0 : __builtin_amdgcn_readfirstlane(
         c0 < a.Iq ? 1 : (c0 < a.Iq + a.Ik ? 2 : 0));
     auto head_pass = [&](int tf, float sa) __attribute__((always_inline)) {
+      // the token's rotate-half table values first, so their loads are in flight while the
+      // pass forms x and the head statistics: first half of the row only (its two halves hold
+      // the same angle); entry [cf][rq] = positions cf * 32 + rq * 8 + 4 g .. + 3 (cf < 2)
+      float4 ct[2][4], st[2][4];
+      if (kRope && hseg != 0) {
+        const int64_t tok = min(m0 + wm * 128 + tf * 32 + fr, a.T - 1);
+        const float* cr = a.cos_tab + tok * a.d;
+        const float* sr = a.sin_tab + tok * a.d;
+        const int ncf = a.d == 64 ? 1 : 2;
+#pragma unroll
+        for (int cf = 0; cf < 2; ++cf)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            if (cf < ncf) {
+              const int j0 = cf * 32 + rq * 8 + g * 4;
+              ct[cf][rq] = *reinterpret_cast<const float4*>(cr + j0);
+              st[cf][rq] = *reinterpret_cast<const float4*>(sr + j0);
+            }
+          }
+      }
       float xv[4][4][4];
 #pragma unroll
       for (int cf = 0; cf < 4; ++cf)
@@ -596,22 +631,20 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
         head_sums(p2, h2);
         r[0] = 1.0f / sqrtf(h2[0] * inv_d + a.h_eps);
         r[1] = 1.0f / sqrtf(h2[1] * inv_d + a.h_eps);
-        const uint16_t* gam = hseg == 1 ? a.hq_gamma : a.hk_gamma;
-        const uint16_t* bet = hseg == 1 ? a.hq_beta : a.hk_beta;
+        const float* gam = &lds_hgb[hseg - 1][0];
+        const float* bet = &lds_hgb[hseg + 1][0];
 #pragma unroll
         for (int cf = 0; cf < 4; ++cf)
 #pragma unroll
           for (int rq = 0; rq < 4; ++rq) {
             // in-head position of the lane's 4 values
             const int p0 = (d64 ? (cf & 1) : cf) * 32 + rq * 8 + g * 4;
-            const uint2 gw = *reinterpret_cast<const uint2*>(gam + p0);
-            const float gv[4] = {bf16_to_f32(gw.x & 0xFFFFu), bf16_to_f32(gw.x >> 16),
-                                 bf16_to_f32(gw.y & 0xFFFFu), bf16_to_f32(gw.y >> 16)};
+            const float4 g4 = *reinterpret_cast<const float4*>(gam + p0);
+            const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (kHead == 2 && bet) {
-              const uint2 bw = *reinterpret_cast<const uint2*>(bet + p0);
-              bv[0] = bf16_to_f32(bw.x & 0xFFFFu); bv[1] = bf16_to_f32(bw.x >> 16);
-              bv[2] = bf16_to_f32(bw.y & 0xFFFFu); bv[3] = bf16_to_f32(bw.y >> 16);
+            if (kHead == 2) {
+              const float4 b4 = *reinterpret_cast<const float4*>(bet + p0);
+              bv[0] = b4.x; bv[1] = b4.y; bv[2] = b4.z; bv[3] = b4.w;
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -619,9 +652,6 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
           }
         if (kRope) {
           // rotate-half pairs (j, j + d/2) with the angle of position j of the token's row
-          const int64_t tok = min(m0 + wm * 128 + tf * 32 + fr, a.T - 1);
-          const float* cr = a.cos_tab + tok * a.d;
-          const float* sr = a.sin_tab + tok * a.d;
           auto rot = [&](int lo, int hi, int rq, float4 c4, float4 s4) __attribute__((always_inline)) {
             const float c[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
@@ -635,19 +665,12 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
 #pragma unroll
             for (int cf = 0; cf < 2; ++cf)
 #pragma unroll
-              for (int rq = 0; rq < 4; ++rq) {
-                const int j0 = cf * 32 + rq * 8 + g * 4;
-                rot(cf, cf + 2, rq, *reinterpret_cast<const float4*>(cr + j0),
-                    *reinterpret_cast<const float4*>(sr + j0));
-              }
+              for (int rq = 0; rq < 4; ++rq) rot(cf, cf + 2, rq, ct[cf][rq], st[cf][rq]);
           } else {
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
-              const int j0 = rq * 8 + g * 4;
-              const float4 c4 = *reinterpret_cast<const float4*>(cr + j0);
-              const float4 s4 = *reinterpret_cast<const float4*>(sr + j0);
-              rot(0, 1, rq, c4, s4);
-              rot(2, 3, rq, c4, s4);
+              rot(0, 1, rq, ct[0][rq], st[0][rq]);
+              rot(2, 3, rq, ct[0][rq], st[0][rq]);
             }
           }
         }

@@ -1,8 +1,8 @@
 """GPU parity of the projection with the per-head qk-norm (RMS_NORM / LAYER_NORM) and
 rotate-half RoPE fused into its epilogue ([QKV-CTE] "Upstream behavior"), against the oracle's
 pass 1 followed by its per-head norm and RoPE (fp64, one bf16 rounding on the GPU side only).
-Covers head_dim 64 and 128, LayerNorm with and without beta, RoPE on and off, GQA, a single
-segment, ragged T and I, T = 1 and both output layouts, with the staged hand-over giving the
+Covers head_dim 64 and 128, LayerNorm with and without beta, RoPE on and off, with and without
+a bias, GQA, a single segment, ragged T and I, T = 1 and both output layouts, with the staged hand-over giving the
 same bytes as the packed rows; and the unsupported shapes."""
 import numpy as np
 import pytest
@@ -16,23 +16,27 @@ pytestmark = pytest.mark.gpu
 
 RMS, LN = 1, 2
 CASES = [
-    # name, projection, kind, rope, beta, layout
-    ("d64-rms-rope", G.custom_projection("hn1", T=128, H=256, nq=2, nkv=2, d=64), RMS, True, False, "bsd"),
-    ("d128-ln-beta-rope-nbsd", G.custom_projection("hn2", T=300, H=512, nq=3, nkv=1, d=128), LN, True, True, "nbsd"),
-    ("d64-rms-T1", G.custom_projection("hn3", T=1, H=256, nq=2, nkv=2, d=64), RMS, False, False, "bsd"),
-    ("single-seg-ln", G.custom_projection("hn4", T=257, H=1024, nq=4, nkv=0, d=128, rope="1d"), LN, True, False, "bsd"),
-    ("gqa-d128-rms", G.custom_projection("hn5", T=700, H=1024, nq=8, nkv=2, d=128), RMS, True, False, "bsd"),
-    ("d64-ln-nbsd", G.custom_projection("hn6", T=130, H=512, nq=6, nkv=2, d=64), LN, False, True, "nbsd"),
+    # name, projection, kind, rope, beta, layout, bias
+    ("d64-rms-rope", G.custom_projection("hn1", T=128, H=256, nq=2, nkv=2, d=64), RMS, True, False, "bsd", True),
+    ("d128-ln-beta-rope-nbsd", G.custom_projection("hn2", T=300, H=512, nq=3, nkv=1, d=128), LN, True, True, "nbsd", True),
+    ("d64-rms-T1", G.custom_projection("hn3", T=1, H=256, nq=2, nkv=2, d=64), RMS, False, False, "bsd", True),
+    ("single-seg-ln", G.custom_projection("hn4", T=257, H=1024, nq=4, nkv=0, d=128, rope="1d"), LN, True, False, "bsd", True),
+    ("gqa-d128-rms", G.custom_projection("hn5", T=700, H=1024, nq=8, nkv=2, d=128), RMS, True, False, "bsd", True),
+    ("d64-ln-nbsd", G.custom_projection("hn6", T=130, H=512, nq=6, nkv=2, d=64), LN, False, True, "nbsd", True),
+    # without a bias (the epilogue's bias-free instantiations)
+    ("d128-rms-rope-nobias", G.custom_projection("hn7", T=300, H=512, nq=3, nkv=1, d=128), RMS, True, False, "bsd", False),
+    ("d64-ln-beta-rope-nobias-nbsd", G.custom_projection("hn8", T=200, H=256, nq=4, nkv=2, d=64), LN, True, True, "nbsd", False),
+    ("single-seg-rms-nobias", G.custom_projection("hn9", T=90, H=256, nq=2, nkv=0, d=128, rope=None), RMS, False, False, "bsd", False),
 ]
 
 
-@pytest.mark.parametrize("name,p,kind,rope,beta,layout", CASES, ids=[c[0] for c in CASES])
-def test_headnorm_parity(name, p, kind, rope, beta, layout):
+@pytest.mark.parametrize("name,p,kind,rope,beta,layout,with_bias", CASES, ids=[c[0] for c in CASES])
+def test_headnorm_parity(name, p, kind, rope, beta, layout, with_bias):
     import torch
     import rope_mxfp8_qkv_amd as q
     q.lib()
     dev = G.torch_dev()
-    inp = G.make_inputs(p)
+    inp = G.make_inputs(p, with_bias=with_bias)
     d = p.head_dim
     rng = np.random.default_rng(17)
     gq = codecs.f64_to_bf16(1 + 0.1 * rng.standard_normal(d))
@@ -54,7 +58,7 @@ def test_headnorm_parity(name, p, kind, rope, beta, layout):
     kw = dict(H=p.H, num_heads=p.num_heads, num_kv_heads=p.num_kv_heads, head_dim=d,
               norm_kind=kind, q_gamma=opt(gq), k_gamma=opt(gk), q_beta=opt(bq), k_beta=opt(bk),
               eps=1e-6, cos=None if cos is None else G.to_dev(cos, dev),
-              sin=None if sin is None else G.to_dev(sin, dev), bias=G.bf16_dev(inp.bias, dev),
+              sin=None if sin is None else G.to_dev(sin, dev), bias=opt(inp.bias),
               layout=q.LAYOUT_NBSD if layout == "nbsd" else q.LAYOUT_BSD)
     q.qkv_rowmx_project_headnorm(G.to_dev(inp.packed, dev), wp, out, workspace=ws, **kw)
     # the staged hand-over of the same codes and scales (the staged encoder matches the oracle's
