@@ -126,12 +126,26 @@ def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy
         per[k] = {"fetch_kib": fk[k], "write_kib": wk[k],
                   "read_bytes": fk[k] * 1024 * fetch_scale, "write_bytes": wk[k] * 1024 * write_scale,
                   "alg_read_bytes": alg[k][0], "alg_write_bytes": alg[k][1]}
+    # the step's two HBM-bound kernels, for comparison with their algorithmic bytes (not part
+    # of the projection call's traffic)
+    Iqk = p.Iq + p.Ik
+    other_alg = {"rmsnorm_quantize_wave_kernel": (4 * T * H + 2 * H, 2 * T * H + T * (H + 4)),
+                 "norm_rope_kernel": (2 * T * Iqk + 8 * T * p.head_dim + 8 * T + 2 * Iqk,
+                                      2 * T * Iqk)}
+    others = {}
+    for k, (ar, aw) in other_alg.items():
+        if k in fk and k in wk:
+            others[k] = {"fetch_kib": fk[k], "write_kib": wk[k],
+                         "read_bytes": fk[k] * 1024 * fetch_scale,
+                         "write_bytes": wk[k] * 1024 * write_scale,
+                         "alg_read_bytes": ar, "alg_write_bytes": aw}
     rec = {"what": f"HBM bytes per dispatch of the projection's kernels ({', '.join(per)}) at "
                    f"T={T} H={H} I={I}, from rocprofv3 FETCH_SIZE/WRITE_SIZE scaled by a "
                    f"{copy_bytes}-byte copy calibration (copy kernel {ck})",
            "kernel_src_sha256_16": source_digest(PROJECT_SRC),
            "fetch_scale": fetch_scale, "write_scale": write_scale, "per_kernel": per,
-           "hbm_bytes_per_call": sum(v["read_bytes"] + v["write_bytes"] for v in per.values())}
+           "hbm_bytes_per_call": sum(v["read_bytes"] + v["write_bytes"] for v in per.values()),
+           "other_step_kernels": others}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps({"traffic_file": TRAFFIC_FILE, "hbm_bytes_per_call": rec["hbm_bytes_per_call"],
