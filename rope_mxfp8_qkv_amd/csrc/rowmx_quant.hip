@@ -256,22 +256,17 @@ __device__ __forceinline__ float wave_max(float v) {
 
 constexpr int kRowsPerWaveBlock = 4;       // rows (wavefronts) per 256-thread block
 
-template <bool RES, bool STAGED, int NC>
-__global__ void __launch_bounds__(64 * kRowsPerWaveBlock) rmsnorm_quantize_wave_kernel(
-    const uint16_t* __restrict__ hid, const uint16_t* __restrict__ res,
-    const uint16_t* __restrict__ gamma, float eps, int64_t T, int64_t H, int64_t Hu,
-    uint16_t* __restrict__ res_out, uint8_t* __restrict__ out, float* __restrict__ row_scale,
-    int KS, int64_t rows) {
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerWaveBlock + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
+// Steps 1-4 of the fused producer for one row on one wavefront (lane l: chunks l + 64 k), into
+// registers y (zeros past H), with the lane's share of max |y| in amax: the arithmetic of
+// normed_row, the fp64 sum by a butterfly inside the wavefront.
+template <bool RES, int NC>
+__device__ __forceinline__ void wave_normed_row(const uint16_t* __restrict__ hid,
+                                                const uint16_t* __restrict__ res,
+                                                const uint16_t* __restrict__ gamma, float eps,
+                                                int64_t H, int64_t Hu,
+                                                uint16_t* __restrict__ res_out, int64_t row,
+                                                int lane, float (&y)[NC][kChunk], float& amax) {
   const int64_t nchunks = H / kChunk;
-  if (STAGED && row >= T) {                 // rows past T up to the tile end: zero codes
-    const StagedRow d = staged_row(out, nullptr, row, KS);
-    for (int64_t c = lane; c < d.padded; c += 64)
-      *reinterpret_cast<u32x2_a4*>(d.chunk(c)) = u32x2_a4{0u, 0u};
-    return;
-  }
   // all of the row's loads first (2 NC x 16 bytes per lane in flight)
   uint4 hv[NC], rv[NC];
 #pragma unroll
@@ -282,7 +277,6 @@ __global__ void __launch_bounds__(64 * kRowsPerWaveBlock) rmsnorm_quantize_wave_
       if (RES) rv[k] = ntload16(res + row * H + c * kChunk);
     }
   }
-  float y[NC][kChunk];
   double ss = 0.0;
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
@@ -314,7 +308,7 @@ __global__ void __launch_bounds__(64 * kRowsPerWaveBlock) rmsnorm_quantize_wave_
   ss = wave_sum(ss);
   // inv = fp32(1 / sqrt(ss / Hu + eps)), sqrt and divide correctly rounded in fp64
   const float inv = (float)(1.0 / sqrt(ss / (double)Hu + (double)eps));
-  float amax = 0.0f;
+  amax = 0.0f;
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
     const int64_t c = lane + 64 * k;
@@ -328,6 +322,27 @@ __global__ void __launch_bounds__(64 * kRowsPerWaveBlock) rmsnorm_quantize_wave_
       }
     }
   }
+}
+
+template <bool RES, bool STAGED, int NC>
+__global__ void __launch_bounds__(64 * kRowsPerWaveBlock) rmsnorm_quantize_wave_kernel(
+    const uint16_t* __restrict__ hid, const uint16_t* __restrict__ res,
+    const uint16_t* __restrict__ gamma, float eps, int64_t T, int64_t H, int64_t Hu,
+    uint16_t* __restrict__ res_out, uint8_t* __restrict__ out, float* __restrict__ row_scale,
+    int KS, int64_t rows) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerWaveBlock + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int64_t nchunks = H / kChunk;
+  if (STAGED && row >= T) {                 // rows past T up to the tile end: zero codes
+    const StagedRow d = staged_row(out, nullptr, row, KS);
+    for (int64_t c = lane; c < d.padded; c += 64)
+      *reinterpret_cast<u32x2_a4*>(d.chunk(c)) = u32x2_a4{0u, 0u};
+    return;
+  }
+  float y[NC][kChunk];
+  float amax;
+  wave_normed_row<RES, NC>(hid, res, gamma, eps, H, Hu, res_out, row, lane, y, amax);
   amax = wave_max(amax);
   // s = fl32(amax / 448); codes = E4M3 RNE saturating of fl32(y / s), formed as
   // fl32(fl64(y * fl64(1 / s))) (exact: see encode_store); a zero row stores s = 0, zero codes
@@ -359,6 +374,83 @@ __global__ void __launch_bounds__(64 * kRowsPerWaveBlock) rmsnorm_quantize_wave_
     if (STAGED) sd.scale(s);
     else *reinterpret_cast<float*>(prow + H) = s;
   }
+}
+
+// The fused MX block-32 producer on one wavefront per row (rows of up to 512 NC elements):
+// wave_normed_row, then each 32-element block (4 consecutive chunks on 4 consecutive lanes) as
+// in mx_encode_codes, the block maximum by two lane exchanges.  Natural layout: the block's
+// first lane stores its exponent byte.  Staged layout: the exponent dword (superstep s, g)
+// holds blocks 8 s + 2 q + g, q = 0..3, which sit on lanes L, L + 8, L + 16, L + 24 of the
+// superstep's 32-lane half (L = 4 g); lane L gathers them by shuffles and stores the dword, 127
+// for blocks past H / 32, as mx_store_exponents_staged does.
+template <bool RES, bool EMIT, bool STAGED, int NC>
+__global__ void __launch_bounds__(64 * kRowsPerWaveBlock) rmsnorm_mx_wave_kernel(
+    const uint16_t* __restrict__ hid, const uint16_t* __restrict__ res,
+    const uint16_t* __restrict__ gamma, float eps, int64_t T, int64_t H, int64_t Hu,
+    uint16_t* __restrict__ res_out, uint8_t* __restrict__ codes, uint8_t* __restrict__ e8,
+    uint16_t* __restrict__ norm_out, int KS, int64_t rows) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerWaveBlock + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int64_t nchunks = H / kChunk;
+  const int S = KS / 4;                     // staged: supersteps of 256 elements
+  uint32_t* const erow = STAGED ? reinterpret_cast<uint32_t*>(e8) +
+                                      ((row / kTileM) * S * kTileM + (row & (kTileM - 1))) * 2
+                                : nullptr;
+  if (STAGED && row >= T) {                 // rows past T up to the tile end
+    const StagedRow d = staged_row(codes, nullptr, row, KS);
+    for (int64_t c = lane; c < d.padded; c += 64)
+      *reinterpret_cast<u32x2_a4*>(d.chunk(c)) = u32x2_a4{0u, 0u};
+    for (int i = lane; i < 2 * S; i += 64) erow[(int64_t)(i >> 1) * kTileM * 2 + (i & 1)] = 0x7F7F7F7Fu;
+    return;
+  }
+  float y[NC][kChunk];
+  float amax_unused;
+  wave_normed_row<RES, NC>(hid, res, gamma, eps, H, Hu, res_out, row, lane, y, amax_unused);
+  StagedRow sd{};
+  if (STAGED) sd = staged_row(codes, nullptr, row, KS);
+  uint8_t* const crow = codes + row * H;
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int64_t c = lane + 64 * k;
+    if (EMIT && c < nchunks)
+      reinterpret_cast<uint4*>(norm_out + row * H)[c] =
+          make_uint4(pack_bf16x2(y[k][0], y[k][1]), pack_bf16x2(y[k][2], y[k][3]),
+                     pack_bf16x2(y[k][4], y[k][5]), pack_bf16x2(y[k][6], y[k][7]));
+    // every lane takes part in the exchanges (a 4-lane group is entirely inside or past H)
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kChunk; ++e) m = fmaxf(m, fabsf(y[k][e]));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    const int eb = (int)((__float_as_uint(m) >> 23) & 0xFFu);
+    const uint32_t E = (uint32_t)max(eb - 8, 0);
+    const float inv = __uint_as_float((254u - E) << 23);          // 2^(127 - E)
+    if (c < nchunks) {
+      uint32_t lo = 0, hi = 0;
+      if (m > 0.0f) {
+        lo = e4m3x4(y[k][0] * inv, y[k][1] * inv, y[k][2] * inv, y[k][3] * inv);
+        hi = e4m3x4(y[k][4] * inv, y[k][5] * inv, y[k][6] * inv, y[k][7] * inv);
+      }
+      __builtin_nontemporal_store(u32x2_t{lo, hi},
+                                  reinterpret_cast<u32x2_t*>(STAGED ? sd.chunk(c)
+                                                                    : crow + c * kChunk));
+      if (!STAGED && (c & 3) == 0) e8[row * (H / 32) + (c >> 2)] = (uint8_t)E;
+    } else if (STAGED && c < sd.padded) {
+      __builtin_nontemporal_store(u32x2_t{0u, 0u}, reinterpret_cast<u32x2_t*>(sd.chunk(c)));
+    }
+    if (STAGED) {
+      const uint32_t el = c < nchunks ? E : 127u;   // blocks past H / 32: 2^0
+      const uint32_t e1 = (uint32_t)__shfl((int)el, lane + 8);
+      const uint32_t e2 = (uint32_t)__shfl((int)el, lane + 16);
+      const uint32_t e3 = (uint32_t)__shfl((int)el, lane + 24);
+      const int in_half = lane & 31;
+      const int sidx = 2 * k + (lane >> 5);
+      if ((in_half == 0 || in_half == 4) && sidx < S)
+        erow[(int64_t)sidx * kTileM * 2 + (in_half >> 2)] = el | (e1 << 8) | (e2 << 16) | (e3 << 24);
+    }
+  }
+  // (every superstep s < S = ceil(H / 256) <= 2 NC has its dwords stored in the loop above)
 }
 
 template <bool RES, bool STAGED>
@@ -667,9 +759,29 @@ template <bool STAGED>
 hipError_t launch_rmsnorm_mx_any(const uint16_t* hid, const uint16_t* res, const uint16_t* gamma,
                                  float eps, int64_t T, int64_t H, int64_t Hu, uint16_t* res_out,
                                  uint8_t* codes, uint8_t* e8, uint16_t* norm_out, hipStream_t s) {
-  const dim3 grid((unsigned)(STAGED ? ceil_div(T, kTileM) * kTileM : T)), block(block_threads(H));
   const int KS = STAGED ? (int)packed_stages(H) : 0;
   const int v = (res ? 2 : 0) | (norm_out ? 1 : 0);
+  // rows of up to 8192 elements: one wavefront per row
+  const int64_t rows = STAGED ? ceil_div(T, kTileM) * kTileM : T;
+  const int64_t nc = ceil_div(H, (int64_t)64 * kChunk);
+  const dim3 wgrid((unsigned)ceil_div(rows, kRowsPerWaveBlock)), wblock(64 * kRowsPerWaveBlock);
+#define QKVMX_MX_WAVE(N)                                                                          \
+  do {                                                                                            \
+    switch (v) {                                                                                  \
+      case 0: hipLaunchKernelGGL((rmsnorm_mx_wave_kernel<false, false, STAGED, N>), wgrid, wblock, 0, s, hid, res, gamma, eps, T, H, Hu, res_out, codes, e8, norm_out, KS, rows); break; \
+      case 1: hipLaunchKernelGGL((rmsnorm_mx_wave_kernel<false, true, STAGED, N>), wgrid, wblock, 0, s, hid, res, gamma, eps, T, H, Hu, res_out, codes, e8, norm_out, KS, rows); break; \
+      case 2: hipLaunchKernelGGL((rmsnorm_mx_wave_kernel<true, false, STAGED, N>), wgrid, wblock, 0, s, hid, res, gamma, eps, T, H, Hu, res_out, codes, e8, norm_out, KS, rows); break; \
+      default: hipLaunchKernelGGL((rmsnorm_mx_wave_kernel<true, true, STAGED, N>), wgrid, wblock, 0, s, hid, res, gamma, eps, T, H, Hu, res_out, codes, e8, norm_out, KS, rows); break; \
+    }                                                                                             \
+    return hipGetLastError();                                                                     \
+  } while (0)
+  if (nc <= 2) QKVMX_MX_WAVE(2);
+  if (nc <= 4) QKVMX_MX_WAVE(4);
+  if (nc <= 8) QKVMX_MX_WAVE(8);
+  if (nc <= 10) QKVMX_MX_WAVE(10);
+  if (nc <= 16) QKVMX_MX_WAVE(16);
+#undef QKVMX_MX_WAVE
+  const dim3 grid((unsigned)(STAGED ? ceil_div(T, kTileM) * kTileM : T)), block(block_threads(H));
   switch (v) {
     case 0: hipLaunchKernelGGL((rmsnorm_mx_kernel<false, false, STAGED>), grid, block, 0, s, hid, res, gamma, eps, T, H, Hu, res_out, codes, e8, norm_out, KS); break;
     case 1: hipLaunchKernelGGL((rmsnorm_mx_kernel<false, true, STAGED>), grid, block, 0, s, hid, res, gamma, eps, T, H, Hu, res_out, codes, e8, norm_out, KS); break;
