@@ -382,7 +382,12 @@ __global__ void __launch_bounds__(64 * kRowsPerWaveBlock) rmsnorm_quantize_wave_
 // first lane stores its exponent byte.  Staged layout: the exponent dword (superstep s, g)
 // holds blocks 8 s + 2 q + g, q = 0..3, which sit on lanes L, L + 8, L + 16, L + 24 of the
 // superstep's 32-lane half (L = 4 g); lane L gathers them by shuffles and stores the dword, 127
-// for blocks past H / 32, as mx_store_exponents_staged does.
+// for blocks past H / 32, as mx_store_exponents_staged does.  Codes go out through ordinary
+// (cached) stores, as in the ROW_MX wave kernel: a 128-byte line of the staged image holds the
+// 64-byte stage segments of two neighbouring rows, both written by the same 4-row block, so L2
+// merges the halves before the line leaves (8-byte streaming stores measured 8% slower at the
+// video shape).  The block-per-row kernel below, whose neighbouring row is another block, keeps
+// streaming stores: ordinary ones measured 3% slower there (H = 16384).
 template <bool RES, bool EMIT, bool STAGED, int NC>
 __global__ void __launch_bounds__(64 * kRowsPerWaveBlock) rmsnorm_mx_wave_kernel(
     const uint16_t* __restrict__ hid, const uint16_t* __restrict__ res,
@@ -432,12 +437,10 @@ __global__ void __launch_bounds__(64 * kRowsPerWaveBlock) rmsnorm_mx_wave_kernel
         lo = e4m3x4(y[k][0] * inv, y[k][1] * inv, y[k][2] * inv, y[k][3] * inv);
         hi = e4m3x4(y[k][4] * inv, y[k][5] * inv, y[k][6] * inv, y[k][7] * inv);
       }
-      __builtin_nontemporal_store(u32x2_t{lo, hi},
-                                  reinterpret_cast<u32x2_t*>(STAGED ? sd.chunk(c)
-                                                                    : crow + c * kChunk));
+      *reinterpret_cast<u32x2_a4*>(STAGED ? sd.chunk(c) : crow + c * kChunk) = u32x2_a4{lo, hi};
       if (!STAGED && (c & 3) == 0) e8[row * (H / 32) + (c >> 2)] = (uint8_t)E;
     } else if (STAGED && c < sd.padded) {
-      __builtin_nontemporal_store(u32x2_t{0u, 0u}, reinterpret_cast<u32x2_t*>(sd.chunk(c)));
+      *reinterpret_cast<u32x2_a4*>(sd.chunk(c)) = u32x2_a4{0u, 0u};
     }
     if (STAGED) {
       const uint32_t el = c < nchunks ? E : 127u;   // blocks past H / 32: 2^0
