@@ -3,7 +3,8 @@ rotate-half RoPE fused into its epilogue ([QKV-CTE] "Upstream behavior"), agains
 pass 1 followed by its per-head norm and RoPE (fp64, one bf16 rounding on the GPU side only).
 Covers head_dim 64 and 128, LayerNorm with and without beta, RoPE on and off, with and without
 a bias, GQA, a single segment, ragged T and I, T = 1 and both output layouts, with the staged hand-over giving the
-same bytes as the packed rows; and the unsupported shapes."""
+same bytes as the packed rows; that only the first half of each table row is read; and the
+unsupported shapes."""
 import numpy as np
 import pytest
 
@@ -75,6 +76,39 @@ def test_headnorm_parity(name, p, kind, rope, beta, layout, with_bias):
         got = oracle.nbsd_to_bsd(got)
     G.check_close(got, ref, f"{name} output")
     assert torch.equal(out_s.view(torch.int16), out.view(torch.int16)), f"{name}: staged != rows"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_headnorm_reads_first_half_of_tables(d):
+    """The rotate-half tables hold each angle in both halves of a row, and the fused path reads
+    the first half only (the contract of qkv_rowmx_project_headnorm): NaN in every second
+    half leaves the output bit for bit unchanged."""
+    import torch
+    import rope_mxfp8_qkv_amd as q
+    q.lib()
+    dev = G.torch_dev()
+    p = G.custom_projection(f"hnh{d}", T=300, H=256, nq=256 // d * 2, nkv=256 // d, d=d)
+    inp = G.make_inputs(p)
+    rng = np.random.default_rng(23)
+    gq = G.bf16_dev(codecs.f64_to_bf16(1 + 0.1 * rng.standard_normal(d)), dev)
+    gk = G.bf16_dev(codecs.f64_to_bf16(1 + 0.1 * rng.standard_normal(d)), dev)
+    wp = q.prepare_weight(G.to_dev(inp.w_codes, dev), G.to_dev(inp.w_e8m0, dev), p.H, p.I)
+    ws = torch.empty(q.qkvmx_workspace_bytes(p.T, p.H, p.I), dtype=torch.uint8, device=dev)
+    cos, sin = G.to_dev(inp.cos, dev), G.to_dev(inp.sin, dev)
+    cos_nan, sin_nan = cos.clone(), sin.clone()
+    cos_nan[:, d // 2:] = float("nan")
+    sin_nan[:, d // 2:] = float("nan")
+    outs = []
+    for c, s_ in ((cos, sin), (cos_nan, sin_nan)):
+        out = torch.empty((p.T, p.I), dtype=torch.bfloat16, device=dev)
+        q.qkv_rowmx_project_headnorm(G.to_dev(inp.packed, dev), wp, out, H=p.H,
+                                     num_heads=p.num_heads, num_kv_heads=p.num_kv_heads,
+                                     head_dim=d, norm_kind=RMS, q_gamma=gq, k_gamma=gk, eps=1e-6,
+                                     cos=c, sin=s_, bias=G.bf16_dev(inp.bias, dev), workspace=ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(outs[0].float()).any()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
 
 
 def test_headnorm_unsupported_shapes():
