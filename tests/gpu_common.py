@@ -206,3 +206,22 @@ def unstage_exp(exp_image, rows: np.ndarray, H: int) -> np.ndarray:
     dw, q = staged_exp_index(rows, H)
     words = exp_image.view(-1).cpu().numpy().view(np.uint32)[dw]
     return ((words >> (8 * q).astype(np.uint32)) & 0xFF).astype(np.uint8)
+
+
+def check_stage_padding(img, T: int, H: int):
+    """Every byte of a staged activation image outside the T x H codes is zero."""
+    n = img.numel()
+    used = np.zeros(n, dtype=bool)
+    used[staged_index(np.arange(T), H).reshape(-1)] = True
+    host = img.cpu().numpy()
+    assert not host[~used].any(), f"{int((host[~used] != 0).sum())} padding bytes are not zero"
+
+
+def check_exp_padding(eimg, T: int, H: int):
+    """Every byte of a staged exponent image outside the T x H/32 exponents is 127 (2^0)."""
+    host = eimg.cpu().numpy().view(np.uint8).reshape(-1)
+    used = np.zeros(host.size, dtype=bool)
+    dw, qb = staged_exp_index(np.arange(T), H)
+    used[(dw * 4 + qb).reshape(-1)] = True
+    bad = host[~used] != 127
+    assert not bad.any(), f"{int(bad.sum())} padding exponents are not 127"
