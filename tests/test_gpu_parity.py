@@ -186,6 +186,13 @@ NR_CASES = [
     ("rope-only", G.custom_projection("ro", T=70, H=256, nq=2, nkv=2, d=64), 4),
     ("k-only", G.custom_projection("ko", T=50, H=256, nq=2, nkv=2, d=64, rope=None), 2),
     ("single-seg", G.custom_projection("sq", T=90, H=256, nq=4, nkv=0, d=64, rope=None), None),
+    # head widths whose d / 16 chunk lanes do not divide the 64 lanes of a token (idle lanes),
+    # the narrowest head (64 head groups per token) and the widest (one group per token)
+    ("d16", G.custom_projection("b16", T=77, H=256, nq=4, nkv=2, d=16), None),
+    ("d48", G.custom_projection("b48", T=130, H=256, nq=5, nkv=3, d=48), None),
+    ("d80-gqa", G.custom_projection("b80", T=61, H=256, nq=6, nkv=2, d=80), None),
+    ("d256", G.custom_projection("b256", T=40, H=256, nq=2, nkv=1, d=256), None),
+    ("d1024", G.custom_projection("b1k", T=9, H=256, nq=2, nkv=1, d=1024), None),
 ]
 
 
