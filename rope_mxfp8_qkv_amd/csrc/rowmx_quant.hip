@@ -3,12 +3,15 @@
 // with one E8M0 exponent per 32 elements; emit_norm_bf16), each optionally fused with the
 // residual add and RMSNorm ([RMSNORM-MX] residual / eps / unpadded_hidden_size).
 //
-// One block per row, two 8-element chunks per thread (H / 16 threads, rounded up to whole
-// wavefronts), the chunks of a thread one block-width apart so each wavefront load covers 1 KiB
-// contiguous.  The row stays in registers between the reduction passes, so every input byte is
-// read from HBM once and every output byte written once (HBM-bound: per row the fused producer
-// moves 4H bytes in and 2H + (H + 4) bytes out).  The packed row is only 4-byte aligned (stride
-// H + 4), so its 8-byte code chunks are stored with dword alignment.
+// Two forms.  The fused producers for rows of up to 8192 elements run one wavefront per row
+// (lane l owns the 8-element chunks l, l + 64, ...; both row reductions are exchanges inside
+// the wavefront, no LDS, no barrier).  Wider rows and the plain encoders run one block per row,
+// two 8-element chunks per thread (H / 16 threads, rounded up to whole wavefronts), the chunks
+// of a thread one block-width apart.  Either way each wavefront load covers 1 KiB contiguous and
+// the row stays in registers between the reduction passes, so every input byte is read from HBM
+// once and every output byte written once (HBM-bound: per row the fused producer moves 4H bytes
+// in and 2H + (H + 4) bytes out).  The packed row is only 4-byte aligned (stride H + 4), so its
+// 8-byte code chunks are stored with dword alignment.
 #include "device_common.h"
 #include "internal.h"
 
