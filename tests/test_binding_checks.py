@@ -121,3 +121,15 @@ def test_norm_rope():
 def test_probe():
     raises(lambda: q.mfma_rate_probe(4, 10, True, z(4 * 255, f32), z((4, 2), i64)), "sink")
     raises(lambda: q.mfma_rate_probe(4, 10, True, z(4 * 256, f32), z((4, 2), f32)), "clocks")
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library every entry point raises: there is no fallback path (the
+    size queries and the operations all go through the one loader)."""
+    from rope_mxfp8_qkv_amd import _abi
+    monkeypatch.setattr(_abi, "_LIB_PATH", str(tmp_path / "libqkvmx.so"))
+    monkeypatch.setattr(_abi, "_lib", None)
+    with pytest.raises(q.QkvmxError, match="is missing"):
+        q.qkv_weight_packed_bytes(H, I)
+    with pytest.raises(q.QkvmxError, match="is missing"):
+        q.lib()
