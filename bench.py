@@ -77,6 +77,109 @@ def copy_calibration(nbytes: int):
     print(json.dumps({"copy_bytes": nbytes, "launches": 3}), flush=True)
 
 
+def power_phases(secs: float):
+    """Back-to-back calls, `secs` seconds each: the staged projection at the full video shape on
+    the workload's codes, the same call on all-zero activation and weight codes, then the MFMA
+    rate probe on random and on zero register operands.  Prints one JSON line per phase start
+    and end (wall-clock seconds) so that board power and clocks sampled by another process
+    (`amd-smi metric -p -c --json` in a loop) can be assigned to the phases; the end line also
+    gives the mean time per call."""
+    import torch
+    import rope_mxfp8_qkv_amd as q
+    dev = torch.device("cuda:0")
+    inp = gen_inputs(5, dev)
+    p = inp["p"]
+    T, H, I = p.T, p.H, p.I
+    codes = torch.empty((H // 4, I, 4), dtype=torch.uint8, device=dev)
+    e8 = torch.empty((H // 32, I), dtype=torch.uint8, device=dev)
+    q.mx_weight_quantize(inp["w"], codes, e8)
+    wp = q.prepare_weight(codes, e8, H, I)
+    wz = q.prepare_weight(torch.zeros_like(codes), e8, H, I)
+    img = torch.empty(q.qkv_act_image_bytes(T, H), dtype=torch.uint8, device=dev)
+    sc = torch.empty((T,), dtype=torch.float32, device=dev)
+    res_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    q.rmsnorm_mx_quantize_staged(inp["hid"], inp["pgamma"], 1e-6, img, sc, residual=inp["res"],
+                                 residual_out=res_out)
+    zimg = torch.zeros_like(img)
+    out = torch.empty((T, I), dtype=torch.bfloat16, device=dev)
+    ssq = torch.empty((T, 2), dtype=torch.float32, device=dev)
+    ws = torch.empty(q.qkv_staged_workspace_bytes(T, I), dtype=torch.uint8, device=dev)
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    clocks = torch.empty((blocks, 2), dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def proj(im, w):
+        q.qkv_rowmx_project_staged(im, sc, w, out, H=H, num_heads=p.num_heads,
+                                   num_kv_heads=p.num_kv_heads, head_dim=p.head_dim,
+                                   bias=inp["bias"], ssq=ssq, workspace=ws)
+
+    def phase(name, fn, per_sync):
+        t0 = time.time()
+        print(json.dumps({"phase": name, "start": t0}), flush=True)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        n = 0
+        while time.time() - t0 < secs:
+            for _ in range(per_sync):
+                fn()
+                n += 1
+            torch.cuda.synchronize()
+        b.record(stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"phase": name, "end": time.time(), "calls": n,
+                          "ms_per_call": a.elapsed_time(b) / n}), flush=True)
+
+    t0 = time.time()
+    time.sleep(min(secs, 3.0))
+    print(json.dumps({"phase": "idle", "start": t0, "end": time.time()}), flush=True)
+    phase("projection_workload_codes", lambda: proj(img, wp), 5)
+    phase("projection_zero_codes", lambda: proj(zimg, wz), 5)
+    phase("mfma_probe_random", lambda: q.mfma_rate_probe(blocks, 20000, True, sink, clocks), 2)
+    phase("mfma_probe_zero", lambda: q.mfma_rate_probe(blocks, 20000, False, sink, clocks), 2)
+
+
+def summarize_power(phases_log: str, samples_file: str, skip_s: float = 1.0):
+    """Mean board power and graphics clock per phase (CPU only) from power_phases' JSON lines and
+    a file of `T <unix time>` lines each followed by one `amd-smi metric -p -c --json` output;
+    the first `skip_s` seconds of each phase are left out (the clock settles)."""
+    import re
+    txt = open(samples_file).read()
+    parts = re.split(r"^T (\d+\.\d+)\n", txt, flags=re.M)
+    samples = []
+    for i in range(1, len(parts), 2):
+        body = parts[i + 1]
+        try:
+            j = json.loads(body[:body.rfind("}") + 1])
+        except ValueError:
+            continue
+        g = j["gpu_data"][0] if isinstance(j, dict) else j[0]
+        gfx = [v["clk"]["value"] for k, v in g["clock"].items()
+               if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)
+               and isinstance(v["clk"].get("value"), (int, float))]
+        samples.append((float(parts[i]), float(g["power"]["socket_power"]["value"]),
+                        sum(gfx) / len(gfx) if gfx else float("nan")))
+    ph = {}
+    for line in open(phases_log):
+        if line.startswith("{"):
+            d = json.loads(line)
+            ph.setdefault(d["phase"], {}).update(d)
+    out = []
+    for name, d in ph.items():
+        sel = [x for x in samples if d["start"] + skip_s <= x[0] <= d["end"]]
+        if not sel:
+            continue
+        out.append({"phase": name, "samples": len(sel),
+                    "power_w": sum(x[1] for x in sel) / len(sel),
+                    "power_w_min": min(x[1] for x in sel), "power_w_max": max(x[1] for x in sel),
+                    "gfx_clock_mhz": sum(x[2] for x in sel) / len(sel),
+                    "ms_per_call": d.get("ms_per_call")})
+    for o in out:
+        print(json.dumps(o))
+    return out
+
+
 PROJECTION_KERNELS = ("act_repack_kernel", "project_kernel", "ssq_reduce_kernel")
 STAGED_KERNELS = ("project_kernel", "ssq_reduce_kernel")   # + a 1-block counter reset
 
@@ -196,6 +299,12 @@ def parse():
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
                                                              "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="only write the traffic record from four rocprofv3 --pmc runs (no GPU)")
+    ap.add_argument("--power-phases", type=float, default=0.0, metavar="SECONDS",
+                    help="only run back-to-back projection calls (workload codes, then zero codes) "
+                         "and MFMA probe calls (random, then zero operands), SECONDS each, printing "
+                         "wall-clock phase markers for an outside power / clock sampler")
+    ap.add_argument("--summarize-power", nargs=2, metavar=("PHASES_LOG", "SAMPLES"),
+                    help="only print mean board power and clock per phase (no GPU)")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30,
                     help="size of the calibration copy the --summarize-traffic runs used")
     return ap.parse_args()
@@ -742,6 +851,12 @@ def main():
         return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.summarize_power:
+        summarize_power(*args.summarize_power)
+        return
+    if args.power_phases:
+        power_phases(args.power_phases)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "the benchmark runs on exactly one GPU; --gpus must be 1 "
