@@ -65,3 +65,34 @@ def test_config_block_entry_divides_by_the_published_peaks():
     assert c["projection_frac_of_peak"] == pytest.approx(2300.0 / 5000.0)
     assert c["norm_rope_hbm_frac"] == pytest.approx(4400.0 / 8000.0)
     assert c["projection_ms"] == 0.28 and c["norm_rope_ms"] == 0.04
+
+
+def test_power_summary_assigns_samples_to_phases(tmp_path, capsys):
+    """--summarize-power: samples inside a phase (after its first second) are averaged; samples
+    outside every phase and a malformed sample are ignored."""
+    import json
+    import bench
+
+    def sample(t, watts, clocks):
+        g = {"gpu": 0, "power": {"socket_power": {"value": watts, "unit": "W"}},
+             "clock": {f"gfx_{i}": {"clk": {"value": c, "unit": "MHz"}} for i, c in enumerate(clocks)}}
+        g["clock"]["mem_0"] = {"clk": {"value": 1900, "unit": "MHz"}}
+        return f"T {t:.6f}\n" + json.dumps({"gpu_data": [g]}, indent=1) + "\n"
+
+    phases = tmp_path / "phases.log"
+    phases.write_text("\n".join(json.dumps(d) for d in [
+        {"phase": "a", "start": 100.0}, {"phase": "a", "end": 104.0, "calls": 10, "ms_per_call": 4.0},
+        {"phase": "b", "start": 104.0}, {"phase": "b", "end": 108.0, "calls": 5, "ms_per_call": 2.0},
+    ]) + "\n[bench] noise\n")
+    samples = tmp_path / "samples.txt"
+    samples.write_text(sample(100.5, 999, [100, 100])            # a's first second: left out
+                       + sample(101.5, 1400, [1700, 1720])
+                       + sample(103.0, 1380, [1740, 1760])
+                       + "T 103.500000\nnot json\n"
+                       + sample(106.0, 700, [2400, 2380])
+                       + sample(120.0, 5, [1, 1]))               # after every phase
+    out = bench.summarize_power(str(phases), str(samples))
+    by = {o["phase"]: o for o in out}
+    assert by["a"]["samples"] == 2 and by["a"]["power_w"] == 1390.0
+    assert by["a"]["gfx_clock_mhz"] == 1730.0 and by["a"]["ms_per_call"] == 4.0
+    assert by["b"]["samples"] == 1 and by["b"]["power_w"] == 700.0 and by["b"]["gfx_clock_mhz"] == 2390.0
