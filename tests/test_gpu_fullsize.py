@@ -183,6 +183,58 @@ def test_fullsize_staged_producer_then_self_attention():
     _run_self_attention(synth.CONFIGS[5].calls[0], producer=True, staged=True)
 
 
+def test_fullsize_nbsd_step_equals_bsd_step():
+    """The benchmark's default step with the NBSd output ([I / d, T, d]; the last heads' rows lie
+    2.3 GB into the output): staged producer -> staged projection -> norm + 3-axis RoPE in
+    NBSd gives byte for byte the BSD step's output re-indexed (every element) and the same sums;
+    sampled rows also against the oracle."""
+    import torch
+    q = __import__("rope_mxfp8_qkv_amd")
+    q.lib()
+    dev = G.torch_dev()
+    gpu = Gpu(q, dev)
+    p = synth.CONFIGS[5].calls[0]
+    rows = sample_rows(p.T)
+    print(f"[fullsize] {p.name} (NBSd vs BSD): T={p.T} H={p.H} I={p.I} rows={len(rows)}", flush=True)
+    hid, res, gam = synth.producer_inputs(p.seed_id, p.T, p.H)
+    img = torch.empty(q.qkv_act_image_bytes(p.T, p.H), dtype=torch.uint8, device=dev)
+    sc = torch.empty((p.T,), dtype=torch.float32, device=dev)
+    res_out = torch.empty((p.T, p.H), dtype=torch.bfloat16, device=dev)
+    q.rmsnorm_mx_quantize_staged(G.bf16_dev(hid, dev), G.bf16_dev(gam, dev), 1e-6, img, sc,
+                                 residual=G.bf16_dev(res, dev), residual_out=res_out)
+    _, packed_ref, _ = oracle.rmsnorm_rowmx(hid[rows], res[rows], gam, 1e-6)
+    del hid, res, res_out
+    w = synth.weight(p)
+    _, _, wp = gpu.weight(w)
+    w_codes, w_e8 = oracle.mx_weight_quantize(w)
+    bias, gq, gk = synth.bias_bf16(p), synth.gamma_bf16(p, "q"), synth.gamma_bf16(p, "k")
+    cos, sin = synth.rope_tables(p)
+    fl = G.flags_of(p)
+    ws = torch.empty(q.qkv_staged_workspace_bytes(p.T, p.I), dtype=torch.uint8, device=dev)
+    d = p.head_dim
+    res = {}
+    for name, layout, shape in (("bsd", q.LAYOUT_BSD, (p.T, p.I)),
+                                ("nbsd", q.LAYOUT_NBSD, (p.I // d, p.T, d))):
+        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        ssq = torch.empty((p.T, 2), dtype=torch.float32, device=dev)
+        q.qkv_rowmx_project_staged(img, sc, wp, out, H=p.H, num_heads=p.num_heads,
+                                   num_kv_heads=p.num_kv_heads, head_dim=d,
+                                   bias=G.bf16_dev(bias, dev), ssq=ssq, workspace=ws,
+                                   layout=layout)
+        q.qk_norm_rope_apply(out, num_heads=p.num_heads, num_kv_heads=p.num_kv_heads,
+                             head_dim=d, eps=1e-6, flags=fl, ssq=ssq,
+                             q_gamma=G.bf16_dev(gq, dev), k_gamma=G.bf16_dev(gk, dev),
+                             cos=G.to_dev(cos, dev), sin=G.to_dev(sin, dev), layout=layout)
+        res[name] = (out, ssq)
+    torch.cuda.synchronize()
+    (bsd, ssq_b), (nbsd, ssq_n) = res["bsd"], res["nbsd"]
+    assert torch.equal(ssq_b.view(torch.int32), ssq_n.view(torch.int32)), "sums differ"
+    nbsd_as_bsd = nbsd.permute(1, 0, 2).reshape(p.T, p.I)
+    assert torch.equal(nbsd_as_bsd.view(torch.int16), bsd.view(torch.int16)), "NBSd != BSD"
+    del bsd
+    check_projection(p, packed_ref, w_codes, w_e8, bias, gq, gk, nbsd_as_bsd, ssq_n, rows, fl)
+
+
 @pytest.mark.parametrize("staged", [False, True], ids=["natural", "staged"])
 def test_fullsize_mx_producer_then_self_attention(staged):
     """MX block-32 path at the full video shape: bf16 hidden + residual -> residual add +
