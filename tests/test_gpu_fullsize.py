@@ -235,6 +235,55 @@ def test_fullsize_nbsd_step_equals_bsd_step():
     check_projection(p, packed_ref, w_codes, w_e8, bias, gq, gk, nbsd_as_bsd, ssq_n, rows, fl)
 
 
+@pytest.mark.parametrize("kind", [1, 2], ids=["rms", "ln-beta"])
+def test_fullsize_headnorm_step(kind):
+    """The benchmark's --headnorm step at the full video shape: staged producer -> staged
+    projection with the per-head RMS_NORM (LAYER_NORM with beta) and 3-axis RoPE fused into its
+    epilogue, no pass 2; per-head gamma / beta as the benchmark draws them (the first head_dim
+    entries of the seeded segment gammas / of the bias); sampled rows against the oracle."""
+    import torch
+    q = __import__("rope_mxfp8_qkv_amd")
+    q.lib()
+    dev = G.torch_dev()
+    gpu = Gpu(q, dev)
+    p = synth.CONFIGS[5].calls[0]
+    d = p.head_dim
+    rows = sample_rows(p.T)
+    print(f"[fullsize] {p.name} (per-head norm kind {kind}): T={p.T} H={p.H} I={p.I} "
+          f"rows={len(rows)}", flush=True)
+    hid, res, gam = synth.producer_inputs(p.seed_id, p.T, p.H)
+    img = torch.empty(q.qkv_act_image_bytes(p.T, p.H), dtype=torch.uint8, device=dev)
+    sc = torch.empty((p.T,), dtype=torch.float32, device=dev)
+    res_out = torch.empty((p.T, p.H), dtype=torch.bfloat16, device=dev)
+    q.rmsnorm_mx_quantize_staged(G.bf16_dev(hid, dev), G.bf16_dev(gam, dev), 1e-6, img, sc,
+                                 residual=G.bf16_dev(res, dev), residual_out=res_out)
+    _, packed_ref, _ = oracle.rmsnorm_rowmx(hid[rows], res[rows], gam, 1e-6)
+    del hid, res, res_out
+    w = synth.weight(p)
+    _, _, wp = gpu.weight(w)
+    w_codes, w_e8 = oracle.mx_weight_quantize(w)
+    bias = synth.bias_bf16(p)
+    hgq, hgk = synth.gamma_bf16(p, "q")[:d], synth.gamma_bf16(p, "k")[:d]
+    hbq, hbk = (bias[:d], bias[d:2 * d]) if kind == 2 else (None, None)
+    cos, sin = synth.rope_tables(p)
+    out = torch.empty((p.T, p.I), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(q.qkv_staged_workspace_bytes(p.T, p.I), dtype=torch.uint8, device=dev)
+    opt = lambda a: None if a is None else G.bf16_dev(a, dev)
+    q.qkv_rowmx_project_headnorm_staged(img, sc, wp, out, H=p.H, num_heads=p.num_heads,
+                                        num_kv_heads=p.num_kv_heads, head_dim=d, norm_kind=kind,
+                                        q_gamma=opt(hgq), k_gamma=opt(hgk), q_beta=opt(hbq),
+                                        k_beta=opt(hbk), eps=1e-6, cos=G.to_dev(cos, dev),
+                                        sin=G.to_dev(sin, dev), bias=opt(bias), workspace=ws)
+    torch.cuda.synchronize()
+    codes, sA = oracle.rowmx_unpack(packed_ref, p.H)
+    X, _ = oracle.project(codes, sA, w_codes, w_e8, None, bias, num_heads=p.num_heads,
+                          num_kv_heads=p.num_kv_heads, head_dim=d)
+    ref = oracle.head_norm_rope(X, kind, hgq, hgk, 1e-6, cos[rows], sin[rows],
+                                num_heads=p.num_heads, num_kv_heads=p.num_kv_heads, head_dim=d,
+                                q_beta_bf16=hbq, k_beta_bf16=hbk)
+    G.check_close(G.bf16_host(out[_idx(rows, dev)]), ref, f"{p.name} per-head output rows")
+
+
 @pytest.mark.parametrize("staged", [False, True], ids=["natural", "staged"])
 def test_fullsize_mx_producer_then_self_attention(staged):
     """MX block-32 path at the full video shape: bf16 hidden + residual -> residual add +
