@@ -147,6 +147,12 @@ __device__ __forceinline__ void dma4g(uint32_t lds, const void* g) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
                :: "s"(lds), "v"(g) : "memory", "m0");
 }
+// 16-byte DMA, scalar base + per-lane offset (lane L: 16 bytes from sbase + voff_L to LDS
+// lds + 16 L).
+__device__ __forceinline__ void dma16(uint32_t lds, const void* sbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(uint32_t lds, const uint8_t* sbase, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
@@ -554,27 +560,53 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
     // boundaries are multiples of 128 channels.
     const int hseg = kHead == 0 ? 0 : __builtin_amdgcn_readfirstlane(
         c0 < a.Iq ? 1 : (c0 < a.Iq + a.Ik ? 2 : 0));
-    auto head_pass = [&](int tf, float sa) __attribute__((always_inline)) {
-      // the token's rotate-half table values first, so their loads are in flight while the
-      // pass forms x and the head statistics: first half of the row only (its two halves hold
-      // the same angle); entry [cf][rq] = positions cf * 32 + rq * 8 + 4 g .. + 3 (cf < 2)
-      float4 ct[2][4], st[2][4];
-      if (kRope && hseg != 0) {
-        const int64_t tok = min(m0 + wm * 128 + tf * 32 + fr, a.T - 1);
-        const float* cr = a.cos_tab + tok * a.d;
-        const float* sr = a.sin_tab + tok * a.d;
-        const int ncf = a.d == 64 ? 1 : 2;
+    // The rotate-half table values of a pass (first half of each token row: its two halves
+    // hold the same angle).  Loaded straight into the MFMA layout, every 16-byte load
+    // instruction would touch 32 token rows (32 cache lines for 1 KiB); instead the two waves
+    // that share a token half (wn = 0, 1) split the tables: wave wn DMA-copies the first 256
+    // bytes of its 32 token rows of cos (wn = 0) or sin (wn = 1) into its own LDS output area,
+    // 4 consecutive rows (8 cache lines) per instruction, token row r at r * 256 bytes with
+    // 16-byte chunk c at position c ^ (r % 16); after a block barrier each wave reads both
+    // tables from the pair's two areas in the MFMA layout (16 lanes: 16 rows, one chunk, every
+    // bank once), and a second barrier frees the areas for the pass's packed x.  Pass 0's copy
+    // goes out before the epilogue's first DMAs, pass tf + 1's after pass tf's read-back, ahead
+    // of its 8 stores.  Only tiles with Q or K channels copy (a block-uniform test, so every
+    // wavefront meets the same barriers).
+    const bool tabs = kRope && kHead != 0 && n0 < a.Iq + a.Ik;
+    float4 ct[2][4], st[2][4];       // entry [cf][rq]: positions cf * 32 + rq * 8 + 4 g .. + 3
+    auto dma_tabs = [&](int tf) __attribute__((always_inline)) {
+      // rows tok0 + r, r < 32, clamped to the last token; the scalar base is the pass's first
+      // row (clamped), so the per-lane offsets stay below 32 rows
+      const int64_t tok0 = m0 + wm * 128 + tf * 32;
+      const int64_t base_tok = min(tok0, a.T - 1);
+      const int last = (int)(a.T - 1 - base_tok);           // rows past it repeat it
+      const float* const tab = (wn == 0 ? a.cos_tab : a.sin_tab) + base_tok * a.d;
+      const uint32_t row_bytes_t = (uint32_t)a.d * 4;
+      const int lv = fresh_lane();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's reads of its area
 #pragma unroll
-        for (int cf = 0; cf < 2; ++cf)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            if (cf < ncf) {
-              const int j0 = cf * 32 + rq * 8 + g * 4;
-              ct[cf][rq] = *reinterpret_cast<const float4*>(cr + j0);
-              st[cf][rq] = *reinterpret_cast<const float4*>(sr + j0);
-            }
-          }
+      for (int k = 0; k < 8; ++k) {
+        const int r = 4 * k + (lv >> 4);
+        const uint32_t voff = (uint32_t)min(r + (int)(tok0 - base_tok), last) * row_bytes_t +
+                              ((uint32_t)((lv & 15) ^ (r & 15)) << 4);
+        dma16(lds_addr(otile) + 1024 * k, tab, voff);
       }
+    };
+    auto tabs_from_lds = [&]() __attribute__((always_inline)) {
+      const uint8_t* const pc = otile - wn * 8192;          // the pair's cos area (wn = 0)
+      const uint8_t* const ps = pc + 8192;                  // its sin area (wn = 1)
+#pragma unroll
+      for (int cf = 0; cf < 2; ++cf)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          if (cf == 0 || a.d == 128) {
+            const int off = fr * 256 + (((cf * 8 + rq * 2 + g) ^ (fr & 15)) << 4);
+            ct[cf][rq] = *reinterpret_cast<const float4*>(pc + off);
+            st[cf][rq] = *reinterpret_cast<const float4*>(ps + off);
+          }
+        }
+    };
+    auto head_pass = [&](int tf, float sa) __attribute__((always_inline)) {
       float xv[4][4][4];
 #pragma unroll
       for (int cf = 0; cf < 4; ++cf)
@@ -686,12 +718,29 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
                                        ((g ^ (fr >> 4)) & 1) * 8) = o;
         }
     };
+    if (tabs) dma_tabs(0);
 #pragma unroll
     for (int tf = 0; tf < 4; ++tf) {
       if (more) {
         if (tf == 0) issue(I0{}, 0);
         if (tf == 1) issue(I1{}, 1);
         if (tf == 2) issue(I2{}, 2);
+      }
+      if (tabs) {
+        // this wave's copy has landed once at most the memory operations issued after it are
+        // outstanding: pass 0: the next tile's stage 0 (2 dword + 8 16-byte DMAs); later passes:
+        // the previous pass's 8 stores and this pass's stage (8 DMAs; none in pass 3)
+        if (tf == 0) {
+          if (more) asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+          else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        } else if (tf < 3) {
+          if (more) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+          else asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+        } else {
+          asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+        }
+        tabs_from_lds();
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
       // this pass's operands to registers first, under one LDS wait: the row scale of this
       // lane's token and the bias (and channel scale) of its 16 channel quads
@@ -764,6 +813,7 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(const ProjectArgs 
         const int row = j * 4 + (el >> 4);
         v[j] = *reinterpret_cast<const uint4*>(otile + row * 256 + ((jc ^ (row & 15)) << 4));
       }
+      if (tabs && tf < 3) dma_tabs(tf + 1);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         // bit 4 of the row is bit 2 of j: those rows hold their 8-byte halves swapped
